@@ -1,0 +1,226 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+A step is one pass of the whole layer -- moe_route -> moe_permute ->
+moe_grouped_ffn -> moe_combine -- over one batch of seeded synthetic input,
+inputs already resident in HBM.  The headline workload is the T=4096 prefill
+(int4 group-32 routed experts, int8 per-row shared expert, bf16 activations,
+d=2560, E=512, top-10 + 1 shared, expert width 1024); the T=16 decode/verify
+batch of the same layer is measured in the same run and reported beside it.
+
+Prints ONE JSON line.  Per-call times come from HIP events recorded on the
+stream the calls are launched on, inside the timed region.  The routed expert
+blobs are rotated over several identical copies so no step can be served from
+the 256 MB last-level cache left warm by the previous one.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+N_ROT = 4                    # routed-blob copies rotated across steps
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=24)
+    return p.parse_args()
+
+
+class Setup:
+    """One layer's weights on the GPU (N_ROT copies of the routed blob)."""
+
+    def __init__(self, cfg, T, torch):
+        import workloads as W
+        from expert_grouped_quantized_amd import make_desc
+        from expert_grouped_quantized_amd.layer import MoELayer, blobs_from_inputs
+        self.cfg, self.T, self.torch = cfg, T, torch
+        t0 = time.time()
+        self.inputs = W.generate(cfg, T=T)
+        self.desc = make_desc(cfg.d, cfg.E, cfg.F, cfg.n_shared, cfg.Fs, act=cfg.act,
+                              expert_w=cfg.expert, shared_w=cfg.shared)
+        routed, shared = blobs_from_inputs(self.desc, self.inputs)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.routed = [dev(routed)]
+        for _ in range(N_ROT - 1):
+            self.routed.append(self.routed[0].clone())
+        self.shared = dev(shared) if shared is not None else None
+        self.wr = dev(self.inputs["wr"].view(np.int16)).view(torch.bfloat16)
+        self.bias = None if self.inputs.get("bias") is None else dev(self.inputs["bias"])
+        self.x = dev(self.inputs["x"].view(np.int16)).view(torch.bfloat16)
+        self.layer = MoELayer(self.desc, cfg.k, T)
+        self.layer.set_weights(self.wr, self.routed[0], self.shared, self.bias)
+        self.routed_bytes = routed.nbytes
+        print(f"[bench] {cfg.name} T={T}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+
+    def step(self, i, ev=None):
+        L = self.layer
+        L.routed_blob = self.routed[i % N_ROT]
+        if ev is not None:
+            ev[0].record()
+        L.route(self.x, self.T)
+        if ev is not None:
+            ev[1].record()
+        L.permute(self.T)
+        if ev is not None:
+            ev[2].record()
+        L.grouped_ffn(self.x, self.T)
+        if ev is not None:
+            ev[3].record()
+        L.combine(self.T)
+        if ev is not None:
+            ev[4].record()
+
+
+def time_steps(S: Setup, steps: int, warmup: int):
+    torch = S.torch
+    for i in range(warmup):
+        S.step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        S.step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = np.zeros(4)
+    for e in evs:
+        per_call += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
+    per_call /= steps
+    layer_ms = np.mean([e[0].elapsed_time(e[4]) for e in evs])
+    return wall, layer_ms, per_call
+
+
+def algorithmic(cfg, T, n_active):
+    """Flops and bytes of one layer call (the definition, not what the kernels move)."""
+    d, F, Fs, k, E = cfg.d, cfg.F, cfg.Fs, cfg.k, cfg.E
+    wbytes = {"i4g32": 0.5 + 2 / 32, "bf16": 2.0, "i8row": 1.0}
+    ffn_flops = 6.0 * T * k * d * F + 6.0 * T * d * Fs
+    router_flops = 2.0 * T * E * d
+    per_expert = 3 * d * F * wbytes[cfg.expert]
+    shared = 3 * d * Fs * wbytes[cfg.shared] + (2 * Fs + d) * 2 * (cfg.shared == "i8row")
+    weight_bytes = n_active * per_expert + shared
+    act = T * d * 2 * 2 + E * d * 2                     # x in, y out, router weights
+    inter = T * k * F * 2 * 2 + T * Fs * 2 * 2 + T * k * d * 4 * 2 + T * d * 4 * 2
+    return dict(ffn_flops=ffn_flops, router_flops=router_flops, weight_bytes=weight_bytes,
+                ffn_bytes=weight_bytes + T * d * 2 + inter - T * d * 4 - T * k * d * 4,
+                layer_bytes=weight_bytes + act + inter)
+
+
+def cpu_baseline(S: Setup, n_tok: int):
+    """The fp64 oracle (never tuned) on a bounded token sample of the same workload."""
+    import oracle
+    cfg, inp = S.cfg, S.inputs
+    fm = {"f32": oracle.F32, "bf16": oracle.BF16, "i4g32": oracle.I4G32, "i8row": oracle.I8ROW}
+    rng = np.random.default_rng(123)
+    tok = np.sort(rng.choice(S.T, size=min(n_tok, S.T), replace=False))
+    spec = dict(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, n_shared=cfg.n_shared, Fs=cfg.Fs,
+                x_fmt=fm[cfg.act], expert_fmt=fm[cfg.expert], shared_fmt=fm[cfg.shared])
+    t0 = time.perf_counter()
+    L = oracle.router_logits(inp["x"], fm[cfg.act], inp["wr"], fm[cfg.act], cfg.d, cfg.E,
+                             bias=inp.get("bias"), tokens=tok)
+    ids, w = oracle.topk_softmax(L, cfg.k)
+    oracle.moe_experts(spec, inp, ids, w, tokens=tok, want_parts=False)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(len(tok) / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(tok)} of the {S.T} tokens of the same seeded workload, whole layer "
+                      f"(fp64 router, top-k, per-expert SwiGLU, shared expert, sum); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    # ---- headline: T=4096 prefill
+    cfg = W.CONFIGS["int4_T4096"]
+    S = Setup(cfg, cfg.T, torch)
+    wall, layer_ms, per_call = time_steps(S, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    n_active = int((np.diff(S.layer.offsets.cpu().numpy()) > 0).sum())
+    A = algorithmic(cfg, cfg.T, n_active)
+    ffn_ms = per_call[2]
+    ffn_tflops = A["ffn_flops"] / (ffn_ms * 1e-3) / 1e12
+    layer_tflops = (A["ffn_flops"] + A["router_flops"]) / (ms_per_step * 1e-3) / 1e12
+    prefill = dict(tokens_per_s=cfg.T / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
+                   layer_event_ms=layer_ms,
+                   call_ms=dict(route=per_call[0], permute=per_call[1], grouped_ffn=per_call[2],
+                                combine=per_call[3]),
+                   layer_tflops=layer_tflops, layer_mfma_frac=layer_tflops / BF16_PEAK_TFLOPS,
+                   layer_gbs=A["layer_bytes"] / (ms_per_step * 1e-3) / 1e9)
+    del S
+    torch.cuda.empty_cache()
+
+    # ---- decode / verify batch, T=16
+    dcfg = W.CONFIGS["int4_decode"]
+    D = Setup(dcfg, 16, torch)
+    dwall, dlayer_ms, dper = time_steps(D, args.decode_steps, 10)
+    d_ms = dwall * 1e3 / args.decode_steps
+    d_active = int((np.diff(D.layer.offsets.cpu().numpy()) > 0).sum())
+    DA = algorithmic(dcfg, 16, d_active)
+    decode = dict(T=16, tokens_per_s=16 / (d_ms * 1e-3), ms_per_step=d_ms, active_experts=d_active,
+                  layer_event_ms=dlayer_ms,
+                  call_ms=dict(route=dper[0], permute=dper[1], grouped_ffn=dper[2], combine=dper[3]),
+                  weight_bytes=DA["weight_bytes"],
+                  layer_hbm_frac=DA["layer_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  ffn_weight_gbs=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(D if False else Setup(cfg, cfg.T, torch), args.cpu_sample_tokens)
+
+    line = {
+        "metric": "MoE-layer tokens/s at T=4096 prefill (int4 g32 experts, int8 shared)",
+        "value": round(prefill["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "moe_layer_int4_T4096_prefill", "T": cfg.T, "d": cfg.d,
+                   "E": cfg.E, "k": cfg.k, "n_shared": cfg.n_shared, "F": cfg.F,
+                   "routed_w": "int4 g32 fp16 scales", "shared_w": "int8 per-row fp16 scales",
+                   "activations": "bf16"},
+        "roofline": {"bound": "mfma", "kernel": "moe_grouped_ffn (gate/up + down GEMMs)",
+                     "achieved": round(ffn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ffn_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "algorithmic_flops_per_launch": A["ffn_flops"],
+                     "avg_launch_ms": round(ffn_ms, 4)},
+        "cpu_baseline": cpu,
+        "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
+        "decode": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in decode.items()},
+    }
+    print(json.dumps(line, default=float), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,479 @@
+// abi.cpp -- the C ABI of include/moe.h: argument checks (host only, before
+// anything is enqueued), the blob packer, workspace sizing and launch dispatch.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_desc(const moe_desc* D) {
+  if (!D) return fail(MOE_EINVAL, "desc is NULL");
+  if (D->n_experts < 1 || D->n_experts > MAX_EXPERTS)
+    return fail(MOE_EINVAL, "n_experts=%d outside [1, %d]", D->n_experts, MAX_EXPERTS);
+  if (D->n_shared != 0 && D->n_shared != 1)
+    return fail(MOE_EINVAL, "n_shared=%d must be 0 or 1", D->n_shared);
+  if (D->d < 1 || D->d > 16384 || D->ffn < 1 || D->ffn > 16384)
+    return fail(MOE_EINVAL, "d=%d / ffn=%d outside [1, 16384]", D->d, D->ffn);
+  if (D->n_shared && (D->shared_ffn < 1 || D->shared_ffn > 16384))
+    return fail(MOE_EINVAL, "shared_ffn=%d outside [1, 16384]", D->shared_ffn);
+  if (D->act == MOE_F32) {
+    if (D->expert_w != MOE_F32 || (D->n_shared && D->shared_w != MOE_F32))
+      return fail(MOE_EUNSUPPORTED, "act F32 needs F32 routed and shared weights");
+    if (D->d % 64 || D->ffn % 64 || (D->n_shared && D->shared_ffn % 64))
+      return fail(MOE_EUNSUPPORTED, "F32 path needs d, ffn, shared_ffn multiples of 64");
+  } else if (D->act == MOE_BF16) {
+    if (D->expert_w != MOE_BF16 && D->expert_w != MOE_I4_G32)
+      return fail(MOE_EUNSUPPORTED, "act BF16 needs routed weights BF16 or I4_G32 (got %d)",
+                  D->expert_w);
+    if (D->n_shared && D->shared_w != MOE_BF16 && D->shared_w != MOE_I8_ROW)
+      return fail(MOE_EUNSUPPORTED, "act BF16 needs shared weights BF16 or I8_ROW (got %d)",
+                  D->shared_w);
+    if (D->d % OUT_COLS_BLOCK || D->ffn % H_COLS_BLOCK ||
+        (D->n_shared && D->shared_ffn % H_COLS_BLOCK))
+      return fail(MOE_EUNSUPPORTED, "BF16 path needs d %% 256 == 0 and ffn, shared_ffn %% 128 == 0");
+  } else {
+    return fail(MOE_EUNSUPPORTED, "act dtype %d unsupported", D->act);
+  }
+  return MOE_OK;
+}
+
+moe_status check_tk(const moe_desc* D, int32_t T, int32_t k) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d is negative", T);
+  if (k < 1 || k > std::min(D->n_experts, MAX_TOPK))
+    return fail(MOE_EINVAL, "k=%d outside [1, min(n_experts, %d)]", k, MAX_TOPK);
+  if ((int64_t)T * k > (int64_t)1 << 30)
+    return fail(MOE_EINVAL, "T*k=%lld exceeds 2^30", (long long)T * k);
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(MOE_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(MOE_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+#define TRY(x)                      \
+  do {                              \
+    moe_status _s = (x);            \
+    if (_s != MOE_OK) return _s;    \
+  } while (0)
+
+moe_status device_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ---- blob packing --------------------------------------------------------
+struct MatIO {
+  int fmt;
+  int64_t rows, K;
+  const uint8_t* q;  // canonical codes / values
+  const uint8_t* s;  // canonical scales (I4: [rows, K/32], I8: [rows])
+};
+
+// canonical element (row, k): code (I4/I8) or raw bits (BF16) / float (F32)
+inline int i4_code(const MatIO& m, int64_t r, int64_t k) {
+  uint8_t b = m.q[r * (m.K / 2) + k / 2];
+  int n = (k & 1) ? (b >> 4) : (b & 15);
+  return n >= 8 ? n - 16 : n;
+}
+inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
+  return ((const uint16_t*)m.s)[r * (m.K / 32) + k / 32];
+}
+
+// One 64-row x 64-K wave tile.  Fragment f (0 or 1) takes its 32 rows from
+// matrix m[f], rows row_of(f, c) for c = 0..31; lane l of the consuming wave
+// holds row c = l % 32, K offsets 8*(l/32) .. +7 of each 16-wide K step.
+struct OutIO {  // canonical outputs of unpacking
+  uint8_t* q;
+  uint8_t* s;
+};
+
+template <typename RowOf>
+bool pack_tile(const MatIO* const m[2], RowOf row_of, int64_t kc, uint8_t* dst) {
+  const int fmt = m[0]->fmt;
+  for (int f = 0; f < 2; f++) {
+    const MatIO& M = *m[f];
+    for (int lane = 0; lane < 64; lane++) {
+      const int64_t r = row_of(f, lane & 31);
+      for (int s = 0; s < 4; s++) {
+        const int64_t k0 = kc * KC + s * 16 + 8 * (lane >> 5);
+        if (fmt == MOE_BF16) {
+          memcpy(dst + ((size_t)(f * 4 + s) * 64 + lane) * 16, (const uint16_t*)M.q + r * M.K + k0, 16);
+        } else if (fmt == MOE_I4_G32) {
+          uint32_t word = 0;  // nibble i = code of element k0 + i, stored as code + 8
+          for (int i = 0; i < 8; i++) {
+            const int c = i4_code(M, r, k0 + i);
+            if (c < -7) return false;
+            word |= (uint32_t)(c + 8) << (4 * i);
+          }
+          memcpy(dst + ((size_t)f * 64 + lane) * 16 + s * 4, &word, 4);
+        } else {  // I8: byte i = code + 128
+          uint8_t* o = dst + ((size_t)(f * 2 + (s >> 1)) * 64 + lane) * 16 + (s & 1) * 8;
+          for (int i = 0; i < 8; i++) o[i] = (uint8_t)((int)((const int8_t*)M.q)[r * M.K + k0 + i] + 128);
+        }
+      }
+    }
+  }
+  if (fmt == MOE_I4_G32) {  // per row c: [frag0 group0, frag0 group1, frag1 group0, frag1 group1]
+    for (int c = 0; c < 32; c++) {
+      uint16_t* o = (uint16_t*)(dst + 2048 + c * 8);
+      for (int f = 0; f < 2; f++)
+        for (int g = 0; g < 2; g++) o[f * 2 + g] = i4_scale(*m[f], row_of(f, c), kc * KC + g * 32);
+    }
+  }
+  return true;
+}
+
+template <typename RowOf>
+void unpack_tile(const MatIO* const m[2], const OutIO out[2], RowOf row_of, int64_t kc,
+                 const uint8_t* src) {
+  const int fmt = m[0]->fmt;
+  for (int f = 0; f < 2; f++) {
+    const int64_t K = m[f]->K;
+    for (int lane = 0; lane < 64; lane++) {
+      const int64_t r = row_of(f, lane & 31);
+      for (int s = 0; s < 4; s++) {
+        const int64_t k0 = kc * KC + s * 16 + 8 * (lane >> 5);
+        if (fmt == MOE_BF16) {
+          memcpy((uint16_t*)out[f].q + r * K + k0, src + ((size_t)(f * 4 + s) * 64 + lane) * 16, 16);
+        } else if (fmt == MOE_I4_G32) {
+          uint32_t word;
+          memcpy(&word, src + ((size_t)f * 64 + lane) * 16 + s * 4, 4);
+          for (int i = 0; i < 8; i++) {
+            const int c = (int)((word >> (4 * i)) & 15) - 8;
+            const int64_t k = k0 + i;
+            uint8_t& b = out[f].q[r * (K / 2) + k / 2];
+            const uint8_t nib = (uint8_t)(c & 15);
+            b = (k & 1) ? (uint8_t)((b & 0x0f) | (nib << 4)) : (uint8_t)((b & 0xf0) | nib);
+          }
+        } else {
+          const uint8_t* o = src + ((size_t)(f * 2 + (s >> 1)) * 64 + lane) * 16 + (s & 1) * 8;
+          for (int i = 0; i < 8; i++) ((int8_t*)out[f].q)[r * K + k0 + i] = (int8_t)((int)o[i] - 128);
+        }
+      }
+    }
+  }
+  if (fmt == MOE_I4_G32) {
+    for (int c = 0; c < 32; c++) {
+      const uint16_t* o = (const uint16_t*)(src + 2048 + c * 8);
+      for (int f = 0; f < 2; f++)
+        for (int g = 0; g < 2; g++)
+          ((uint16_t*)out[f].s)[row_of(f, c) * (m[f]->K / 32) + 2 * kc + g] = o[f * 2 + g];
+    }
+  }
+}
+
+size_t canon_q_bytes(int fmt, int64_t rows, int64_t K) {
+  switch (fmt) {
+    case MOE_F32: return rows * K * 4;
+    case MOE_BF16: return rows * K * 2;
+    case MOE_I4_G32: return rows * K / 2;
+    default: return rows * K;
+  }
+}
+size_t canon_s_bytes(int fmt, int64_t rows, int64_t K) {
+  return fmt == MOE_I4_G32 ? rows * (K / 32) * 2 : fmt == MOE_I8_ROW ? rows * 2 : 0;
+}
+
+struct ExpertIO {  // canonical pointers of one expert (gate, up, down)
+  const uint8_t *g, *gs, *u, *us, *dn, *ds;
+};
+
+// Pack (or, with unpack = true, unpack) one expert.  Returns false on a -8 code.
+bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool unpack) {
+  const size_t w1b = w1_bytes(fmt, d, F);
+  if (fmt == MOE_F32) {
+    if (!unpack) {
+      memcpy(blob, io.g, F * d * 4);
+      memcpy(blob + F * d * 4, io.u, F * d * 4);
+      memcpy(blob + w1b, io.dn, d * F * 4);
+    } else {
+      memcpy((void*)io.g, blob, F * d * 4);
+      memcpy((void*)io.u, blob + F * d * 4, F * d * 4);
+      memcpy((void*)io.dn, blob + w1b, d * F * 4);
+    }
+    return true;
+  }
+  const size_t tb = tile_bytes(fmt);
+  const int64_t nk1 = d / KC, nk2 = F / KC;
+  const MatIO G{fmt, F, d, io.g, io.gs}, U{fmt, F, d, io.u, io.us}, Dn{fmt, d, F, io.dn, io.ds};
+  // W1 wave tile (nb, w): frag 0 = gate rows, frag 1 = up rows nb*128 + w*32 + c
+  const MatIO* const m1[2] = {&G, &U};
+  const OutIO o1[2] = {{(uint8_t*)io.g, (uint8_t*)io.gs}, {(uint8_t*)io.u, (uint8_t*)io.us}};
+  for (int64_t nb = 0; nb < F / H_COLS_BLOCK; nb++) {
+    for (int w = 0; w < WAVES; w++) {
+      const int64_t rbase = nb * H_COLS_BLOCK + w * 32;
+      auto row_of = [rbase](int, int c) { return rbase + c; };
+      for (int64_t kc = 0; kc < nk1; kc++) {
+        uint8_t* t = blob + ((size_t)(nb * WAVES + w) * nk1 + kc) * tb;
+        if (!unpack) {
+          if (!pack_tile(m1, row_of, kc, t)) return false;
+        } else {
+          unpack_tile(m1, o1, row_of, kc, t);
+        }
+      }
+    }
+  }
+  // W2 wave tile (nb, w): frag f = down rows nb*256 + w*64 + f*32 + c
+  uint8_t* w2 = blob + w1b;
+  const MatIO* const m2[2] = {&Dn, &Dn};
+  const OutIO o2[2] = {{(uint8_t*)io.dn, (uint8_t*)io.ds}, {(uint8_t*)io.dn, (uint8_t*)io.ds}};
+  for (int64_t nb = 0; nb < d / OUT_COLS_BLOCK; nb++) {
+    for (int w = 0; w < WAVES; w++) {
+      const int64_t rbase = nb * OUT_COLS_BLOCK + w * 64;
+      auto row_of = [rbase](int f, int c) { return rbase + f * 32 + c; };
+      for (int64_t kc = 0; kc < nk2; kc++) {
+        uint8_t* t = w2 + ((size_t)(nb * WAVES + w) * nk2 + kc) * tb;
+        if (!unpack) {
+          if (!pack_tile(m2, row_of, kc, t)) return false;
+        } else {
+          unpack_tile(m2, o2, row_of, kc, t);
+        }
+      }
+    }
+  }
+  if (fmt == MOE_I8_ROW) {  // row scales after the tiles of each section
+    uint8_t* s1 = blob + (2 * F / 64) * nk1 * tb;
+    uint8_t* s2 = w2 + (d / 64) * nk2 * tb;
+    if (!unpack) {
+      memcpy(s1, io.gs, F * 2);
+      memcpy(s1 + F * 2, io.us, F * 2);
+      memcpy(s2, io.ds, d * 2);
+    } else {
+      memcpy((void*)io.gs, s1, F * 2);
+      memcpy((void*)io.us, s1 + F * 2, F * 2);
+      memcpy((void*)io.ds, s2, d * 2);
+    }
+  }
+  return true;
+}
+
+moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, const void* gs,
+                          const void* up, const void* us, const void* down, const void* ds,
+                          void* blob, size_t blob_bytes, bool unpack) {
+  TRY(check_desc(D));
+  if (kind != MOE_BLOB_ROUTED && kind != MOE_BLOB_SHARED)
+    return fail(MOE_EINVAL, "blob kind %d unknown", kind);
+  if (kind == MOE_BLOB_SHARED && !D->n_shared)
+    return fail(MOE_EINVAL, "desc has no shared expert");
+  const int fmt = kind == MOE_BLOB_ROUTED ? D->expert_w : D->shared_w;
+  const int64_t n = kind == MOE_BLOB_ROUTED ? D->n_experts : 1;
+  const int64_t d = D->d, F = kind == MOE_BLOB_ROUTED ? D->ffn : D->shared_ffn;
+  const size_t need = n * expert_bytes(fmt, d, F);
+  if (!blob || !gate || !up || !down) return fail(MOE_EINVAL, "NULL weight or blob pointer");
+  if ((fmt == MOE_I4_G32 || fmt == MOE_I8_ROW) && (!gs || !us || !ds))
+    return fail(MOE_EINVAL, "quantized weights need their scales");
+  if (blob_bytes < need) return fail(MOE_EINVAL, "blob_bytes %zu < %zu", blob_bytes, need);
+  const size_t gq = canon_q_bytes(fmt, F, d), gsb = canon_s_bytes(fmt, F, d);
+  const size_t dq = canon_q_bytes(fmt, d, F), dsb = canon_s_bytes(fmt, d, F);
+  const size_t eb = expert_bytes(fmt, d, F);
+  std::vector<char> bad(n, 0);
+  auto work = [&](int64_t e0, int64_t e1) {
+    for (int64_t e = e0; e < e1; e++) {
+      ExpertIO io{(const uint8_t*)gate + e * gq, gs ? (const uint8_t*)gs + e * gsb : nullptr,
+                  (const uint8_t*)up + e * gq,   us ? (const uint8_t*)us + e * gsb : nullptr,
+                  (const uint8_t*)down + e * dq, ds ? (const uint8_t*)ds + e * dsb : nullptr};
+      if (!pack_expert(fmt, d, F, io, (uint8_t*)blob + e * eb, unpack)) bad[e] = 1;
+    }
+  };
+  const int nt = (int)std::max<int64_t>(1, std::min<int64_t>(n, std::max(1u, std::thread::hardware_concurrency())));
+  std::vector<std::thread> th;
+  for (int i = 0; i < nt; i++) th.emplace_back(work, n * i / nt, n * (i + 1) / nt);
+  for (auto& t : th) t.join();
+  for (int64_t e = 0; e < n; e++)
+    if (bad[e]) return fail(MOE_EINVAL, "expert %lld holds an int4 code -8 (codes must be in [-7, 7])", (long long)e);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EDEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_blob_bytes(const moe_desc* D, int32_t kind, size_t* bytes) {
+  TRY(check_desc(D));
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  if (kind == MOE_BLOB_ROUTED) {
+    *bytes = (size_t)D->n_experts * expert_bytes(D->expert_w, D->d, D->ffn);
+  } else if (kind == MOE_BLOB_SHARED) {
+    *bytes = D->n_shared ? expert_bytes(D->shared_w, D->d, D->shared_ffn) : 0;
+  } else {
+    return fail(MOE_EINVAL, "blob kind %d unknown", kind);
+  }
+  return ok();
+}
+
+moe_status moe_pack_experts(const moe_desc* D, int32_t kind, const void* gate, const void* gs,
+                            const void* up, const void* us, const void* down, const void* ds,
+                            void* blob, size_t blob_bytes) {
+  return pack_or_unpack(D, kind, gate, gs, up, us, down, ds, blob, blob_bytes, false);
+}
+
+moe_status moe_unpack_experts(const moe_desc* D, int32_t kind, const void* blob, size_t blob_bytes,
+                              void* gate, void* gs, void* up, void* us, void* down, void* ds) {
+  return pack_or_unpack(D, kind, gate, gs, up, us, down, ds, (void*)blob, blob_bytes, true);
+}
+
+moe_status moe_workspace_bytes(const moe_desc* D, int32_t T, int32_t k, size_t* bytes) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  *bytes = ws_layout(*D, T, k).total;
+  return ok();
+}
+
+moe_status moe_route(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
+                     const void* router_w, const float* bias, float* logits, int32_t* topk_ids,
+                     float* topk_w, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(hidden, "hidden"));
+  TRY(check_ptr(router_w, "router_w"));
+  if (bias) TRY(check_ptr(bias, "bias", 4));
+  TRY(check_ptr(logits, "logits"));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_w, "topk_w"));
+  if (T == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = D->act == MOE_F32
+                     ? launch_router_f32(T, D->d, D->n_experts, (const float*)hidden,
+                                         (const float*)router_w, bias, logits, s)
+                     : launch_router_bf16(T, D->d, D->n_experts, hidden, router_w, bias, logits, s);
+  if (e != hipSuccess) return device_result(e, "router launch");
+  return device_result(launch_topk(T, D->n_experts, k, logits, topk_ids, topk_w, s),
+                       "top-k launch");
+}
+
+moe_status moe_route_from_logits(const moe_desc* D, int32_t T, int32_t k, const float* logits,
+                                 int32_t* topk_ids, float* topk_w, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(logits, "logits"));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_w, "topk_w"));
+  if (T == 0) return ok();
+  return device_result(
+      launch_topk(T, D->n_experts, k, logits, topk_ids, topk_w, (hipStream_t)stream),
+      "top-k launch");
+}
+
+moe_status moe_permute(const moe_desc* D, int32_t T, int32_t k, const int32_t* topk_ids,
+                       int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(offsets, "offsets"));
+  TRY(check_ptr(perm, "perm"));
+  TRY(check_ptr(inv_perm, "inv_perm"));
+  TRY(check_ptr(workspace, "workspace", 256));
+  const WsLayout L = ws_layout(*D, T, k);
+  if (ws_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if (T == 0) return ok();
+  return device_result(launch_plan(T * k, D->n_experts, topk_ids, offsets, perm, inv_perm,
+                                   workspace, L, (hipStream_t)stream),
+                       "route-plan launch");
+}
+
+moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
+                           const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                           const void* routed_blob, const void* shared_blob, float* out_assign,
+                           float* shared_out, void* workspace, size_t ws_bytes, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(hidden, "hidden"));
+  TRY(check_ptr(topk_w, "topk_w"));
+  TRY(check_ptr(offsets, "offsets"));
+  TRY(check_ptr(perm, "perm"));
+  TRY(check_ptr(routed_blob, "routed_blob"));
+  TRY(check_ptr(out_assign, "out_assign"));
+  TRY(check_ptr(workspace, "workspace", 256));
+  if (D->n_shared) {
+    TRY(check_ptr(shared_blob, "shared_blob"));
+    TRY(check_ptr(shared_out, "shared_out"));
+  } else if (shared_blob || shared_out) {
+    return fail(MOE_EINVAL, "shared_blob/shared_out must be NULL when n_shared == 0");
+  }
+  const WsLayout L = ws_layout(*D, T, k);
+  if (ws_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if (T == 0) return ok();
+  uint8_t* w = (uint8_t*)workspace;
+  FfnArgs a{};
+  a.T = T; a.k = k; a.d = D->d; a.E = D->n_experts; a.F = D->ffn;
+  a.Fs = D->n_shared ? D->shared_ffn : 0; a.n_shared = D->n_shared;
+  a.routed_fmt = D->expert_w; a.shared_fmt = D->shared_w;
+  a.routed_slots = L.routed_slots;
+  a.shared_slots = D->n_shared ? (T + BM - 1) / BM : 0;
+  a.hidden = hidden; a.topk_w = topk_w; a.offsets = offsets; a.perm = perm;
+  a.ntiles = (const int32_t*)(w + L.ntiles);
+  a.tiles = (const int2*)(w + L.tiles);
+  a.routed_blob = (const uint8_t*)routed_blob;
+  a.shared_blob = (const uint8_t*)shared_blob;
+  a.h_routed = w + L.h_routed; a.h_shared = w + L.h_shared;
+  a.out_assign = out_assign; a.shared_out = shared_out;
+  hipStream_t s = (hipStream_t)stream;
+  return device_result(D->act == MOE_F32 ? launch_ffn_f32(a, s) : launch_ffn_bf16(a, s),
+                       "grouped-ffn launch");
+}
+
+moe_status moe_combine(const moe_desc* D, int32_t T, int32_t k, const float* out_assign,
+                       const int32_t* inv_perm, const float* shared_out, void* y, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(out_assign, "out_assign"));
+  TRY(check_ptr(inv_perm, "inv_perm"));
+  TRY(check_ptr(y, "y"));
+  if (D->n_shared) TRY(check_ptr(shared_out, "shared_out"));
+  else if (shared_out) return fail(MOE_EINVAL, "shared_out must be NULL when n_shared == 0");
+  if (T == 0) return ok();
+  return device_result(launch_combine(T, k, D->d, D->act, out_assign, inv_perm, shared_out, y,
+                                      (hipStream_t)stream),
+                       "combine launch");
+}
+
+}  // extern "C"

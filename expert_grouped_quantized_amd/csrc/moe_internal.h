@@ -1,0 +1,124 @@
+// moe_internal.h -- layout constants and launch entry points shared by the
+// host side (abi.cpp, the packer) and the HIP kernels.  Not installed; the
+// public interface is include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---- tiling of the expert-grouped GEMMs (bf16 MFMA 32x32x16) -------------
+// A block is 4 wave64s.  It owns up to BM rows of one expert's group and
+// BN_WAVE columns per wave:
+//   stage 1 (gate/up): each wave owns 32 h columns = 32 gate rows + 32 up rows
+//                      of W1, so a block makes 128 h columns;
+//   stage 2 (down):    each wave owns 64 output columns, a block 256.
+// K advances in chunks of KC; one chunk of one wave's 64 weight rows is a
+// "wave tile", stored contiguously in the blob.
+constexpr int BM = 128;          // rows of an expert group per block (4 x 32)
+constexpr int KC = 64;           // K per chunk (4 MFMA K-steps of 16)
+constexpr int WAVES = 4;         // waves per GEMM block
+constexpr int H_COLS_BLOCK = 128;  // stage-1 h columns per block
+constexpr int OUT_COLS_BLOCK = 256;  // stage-2 output columns per block
+
+// wave-tile bytes (64 weight rows x 64 K) per stored format
+constexpr int TILE_BYTES_BF16 = 64 * 64 * 2;        // 8192
+constexpr int TILE_BYTES_I4 = 64 * 64 / 2 + 64 * 2 * 2;  // 2048 codes + 256 scales
+constexpr int TILE_BYTES_I8 = 64 * 64;              // 4096 (row scales kept apart)
+
+// ---- route plan ----------------------------------------------------------
+constexpr int PLAN_CHUNK = 4096;   // assignments per block of the plan kernels
+constexpr int PLAN_THREADS = 1024; // 16 waves
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_TOPK = 32;
+
+__host__ __device__ inline size_t tile_bytes(int fmt) {
+  return fmt == MOE_BF16 ? TILE_BYTES_BF16 : fmt == MOE_I4_G32 ? TILE_BYTES_I4 : TILE_BYTES_I8;
+}
+
+// Bytes of the W1 (gate/up, [2F, d]) and W2 (down, [d, F]) sections of one
+// expert in the device blob.
+__host__ __device__ inline size_t w1_bytes(int fmt, size_t d, size_t F) {
+  if (fmt == MOE_F32) return 2 * F * d * 4;
+  size_t tiles = (2 * F / 64) * (d / KC) * tile_bytes(fmt);  // 64-row wave tiles
+  return tiles + (fmt == MOE_I8_ROW ? 2 * F * 2 : 0);
+}
+__host__ __device__ inline size_t w2_bytes(int fmt, size_t d, size_t F) {
+  if (fmt == MOE_F32) return d * F * 4;
+  size_t tiles = (d / 64) * (F / KC) * tile_bytes(fmt);
+  return tiles + (fmt == MOE_I8_ROW ? d * 2 : 0);
+}
+__host__ __device__ inline size_t expert_bytes(int fmt, size_t d, size_t F) {
+  return w1_bytes(fmt, d, F) + w2_bytes(fmt, d, F);
+}
+
+// Workspace layout, shared by moe_workspace_bytes, moe_permute and
+// moe_grouped_ffn.  Every region starts on a 256-byte boundary.
+struct WsLayout {
+  int n_chunks;        // plan blocks
+  int routed_slots;    // upper bound on routed row tiles
+  size_t counts;       // int32 [n_chunks][E]   per-chunk expert histogram
+  size_t ntiles;       // int32 [1]             routed row tiles in the plan
+  size_t tiles;        // int2  [routed_slots]  (expert, first row) per tile
+  size_t h_routed;     // act-typed [T*k, F]    intermediate h, permuted rows
+  size_t h_shared;     // act-typed [T, Fs]     intermediate h of the shared expert
+  size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
+  WsLayout L{};
+  int64_t n = T * k;
+  L.n_chunks = (int)((n + PLAN_CHUNK - 1) / PLAN_CHUNK);
+  int64_t bound = (n + BM - 1) / BM + (n < D.n_experts ? n : D.n_experts);
+  L.routed_slots = (int)(bound < n ? bound : n);
+  size_t elem = D.act == MOE_F32 ? 4 : 2;
+  size_t off = 0;
+  L.counts = off;   off = align256(off + (size_t)L.n_chunks * D.n_experts * 4);
+  L.ntiles = off;   off = align256(off + 4);
+  L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 8);
+  L.h_routed = off; off = align256(off + (size_t)n * D.ffn * elem);
+  L.h_shared = off; off = align256(off + (D.n_shared ? (size_t)T * D.shared_ffn * elem : 0));
+  L.total = off;
+  return L;
+}
+
+// ---- launches (each returns the HIP error of its launch) ------------------
+hipError_t launch_router_bf16(int T, int d, int E, const void* x, const void* wr, const float* bias,
+                              float* logits, hipStream_t s);
+hipError_t launch_router_f32(int T, int d, int E, const float* x, const float* wr,
+                             const float* bias, float* logits, hipStream_t s);
+hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w,
+                       hipStream_t s);
+hipError_t launch_plan(int n, int E, const int32_t* ids, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_perm, void* ws, const WsLayout& L, hipStream_t s);
+
+struct FfnArgs {
+  int T, k, d, E, F, Fs, n_shared;
+  int routed_fmt, shared_fmt;
+  int routed_slots, shared_slots;
+  const void* hidden;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* ntiles;
+  const int2* tiles;
+  const uint8_t* routed_blob;
+  const uint8_t* shared_blob;
+  void* h_routed;
+  void* h_shared;
+  float* out_assign;
+  float* shared_out;
+};
+hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,
+                          const int32_t* inv_perm, const float* shared_out, void* y,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of the expert-grouped, group-quantized MoE layer for MI355X.
+ *
+ * The layer (pages on serving Qwen3.8-Flash-Next):
+ *   - TandemLLM docs, chapter 17 "Qwen3.8-Flash-Next", Table 17.1: 512 routed
+ *     experts a layer; every token runs 10 of them plus 1 shared expert.
+ *   - "Qwen3.8-Flash-Next-Dual-GPU" README, section "Dedicated prefill lane":
+ *     build a deterministic expert-major route plan on the GPU (moe_permute),
+ *     run the matrix work expert by expert on 4/8-bit weights with 16-bit
+ *     activations, fold the router weights into the intermediate activation,
+ *     write one FP32 output per assignment (moe_grouped_ffn), and reduce each
+ *     token's routes in a fixed order without atomics (moe_combine).
+ *   - same README, section "Independent decode lane": the 512-expert router
+ *     uses a deterministic stable top-k (moe_route).
+ *   - same README, "Model artifact and memory placement" table: routed experts
+ *     stored as symmetric grouped int4/int8, the router kept unquantized.
+ *
+ * Conventions for every call below:
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates device memory and keeps no device state between calls.
+ *   - Device calls (moe_route*, moe_permute, moe_grouped_ffn, moe_combine)
+ *     take device pointers and a hipStream_t passed as `void* stream` (NULL =
+ *     the null stream).  They only enqueue work: nothing synchronizes, so the
+ *     four calls can be captured in one HIP graph.  They run on the device
+ *     current to the calling thread.
+ *   - Errors: arguments are checked on the host before anything is enqueued.
+ *     A failed check returns a negative moe_status and sets a thread-local
+ *     message (moe_last_error).  A launch failure returns MOE_EDEVICE.  T == 0
+ *     returns MOE_OK and enqueues nothing.  Values inside device buffers (for
+ *     example expert ids) are preconditions and are not checked.
+ *   - Alignment: every device pointer must be 16-byte aligned; the workspace
+ *     256-byte aligned.
+ *   - Reentrancy: calls are thread-safe; concurrent calls need distinct
+ *     workspaces and outputs.
+ *
+ * Canonical weight layouts (what moe_pack_experts reads), per expert, experts
+ * stacked contiguously:
+ *   gate [F, d], up [F, d], down [d, F]   row-major, K (the reduced dim) last.
+ *   MOE_F32 / MOE_BF16: one element per weight.
+ *   MOE_I4_G32: symmetric int4, two's complement, codes in [-7, 7]; byte j of a
+ *     row holds element 2j in its low nibble and 2j+1 in its high nibble; one
+ *     fp16 scale per 32 consecutive elements along K, scales [rows, K/32].
+ *     Weight value = code * scale.
+ *   MOE_I8_ROW: int8 codes in [-127, 127], one fp16 scale per row, scales [rows].
+ * The device blob written by moe_pack_experts is a private, tile-ordered
+ * layout; its only contract is moe_pack_experts / moe_unpack_experts.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument: null pointer, bad size, misalignment */
+  MOE_EUNSUPPORTED = -2, /* valid request that this library does not implement */
+  MOE_EWORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes()        */
+  MOE_EDEVICE = -4       /* the HIP runtime reported an error                   */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,    /* IEEE binary32                                     */
+  MOE_BF16 = 1,   /* bfloat16                                          */
+  MOE_I4_G32 = 2, /* symmetric int4 + fp16 scale per 32 along K        */
+  MOE_I8_ROW = 3  /* symmetric int8 + fp16 scale per output row        */
+} moe_dtype;
+
+typedef enum moe_blob_kind {
+  MOE_BLOB_ROUTED = 0, /* the n_experts routed experts */
+  MOE_BLOB_SHARED = 1  /* the shared expert            */
+} moe_blob_kind;
+
+/* Shape and storage of one MoE layer.
+ * Supported combinations:
+ *   act MOE_F32 : expert_w MOE_F32, shared_w MOE_F32 (router fp32, y fp32)
+ *   act MOE_BF16: expert_w MOE_BF16 or MOE_I4_G32,
+ *                 shared_w MOE_BF16 or MOE_I8_ROW  (router bf16, y bf16)
+ * Sizes: 1 <= n_experts <= 1024; n_shared 0 or 1.  For act MOE_BF16:
+ * d % 256 == 0, ffn % 128 == 0, shared_ffn % 128 == 0.  For act MOE_F32:
+ * d, ffn, shared_ffn multiples of 64.  d, ffn, shared_ffn <= 16384.         */
+typedef struct moe_desc {
+  int32_t d;          /* hidden width                                       */
+  int32_t n_experts;  /* E, routed experts                                  */
+  int32_t ffn;        /* F, SwiGLU width of a routed expert                 */
+  int32_t n_shared;   /* 0 or 1 always-active shared expert                 */
+  int32_t shared_ffn; /* Fs, SwiGLU width of the shared expert (0 if none)  */
+  int32_t act;        /* moe_dtype of hidden, router weights and y          */
+  int32_t expert_w;   /* moe_dtype of the routed expert weights             */
+  int32_t shared_w;   /* moe_dtype of the shared expert weights             */
+} moe_desc;
+
+/* ---------------------------------------------------------------- host only */
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+/* Static text for a status code ("ok", "invalid argument", ...). */
+const char* moe_status_str(int32_t status);
+
+/* Thread-local text describing the last failed call on this thread ("" if
+ * none).  Valid until the next library call on the same thread.            */
+const char* moe_last_error(void);
+
+/* Bytes of the device blob that holds the routed experts (kind ROUTED) or the
+ * shared expert (kind SHARED) of `desc`.  Host only, no GPU touched.        */
+moe_status moe_blob_bytes(const moe_desc* desc, int32_t kind, size_t* bytes);
+
+/* Pack canonical weights (layouts above; `*_scales` NULL for F32/BF16) into
+ * the private device blob, written to the host buffer `blob` of `blob_bytes`
+ * (>= moe_blob_bytes).  The caller copies it to device memory.  For ROUTED the
+ * inputs hold n_experts experts stacked; for SHARED one expert.
+ * MOE_I4_G32 codes must lie in [-7, 7] (symmetric); an 8 (-8) code returns
+ * MOE_EINVAL.  Host only.                                                   */
+moe_status moe_pack_experts(const moe_desc* desc, int32_t kind, const void* gate,
+                            const void* gate_scales, const void* up, const void* up_scales,
+                            const void* down, const void* down_scales, void* blob,
+                            size_t blob_bytes);
+
+/* Inverse of moe_pack_experts: canonical weights from a host copy of a blob
+ * (outputs sized as the canonical inputs; `*_scales` ignored for F32/BF16). */
+moe_status moe_unpack_experts(const moe_desc* desc, int32_t kind, const void* blob,
+                              size_t blob_bytes, void* gate, void* gate_scales, void* up,
+                              void* up_scales, void* down, void* down_scales);
+
+/* Bytes of device workspace that moe_permute and moe_grouped_ffn need for T
+ * tokens and top-k.  Host only.                                             */
+moe_status moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t k, size_t* bytes);
+
+/* ------------------------------------------------------------------ device */
+
+/* Router and stable top-k ("Independent decode lane").
+ *   hidden    [T, d]  act dtype, row-major
+ *   router_w  [E, d]  act dtype, row-major (never quantized)
+ *   bias      [E] fp32 added to every logit, or NULL
+ *   logits    [T, E] fp32 out: sum_i hidden[t,i]*router_w[e,i] (+ bias[e]),
+ *             accumulated in fp32
+ *   topk_ids  [T, k] int32 out: per token the k experts in order of (logit
+ *             descending, expert id ascending); -0.0 ties +0.0
+ *   topk_w    [T, k] fp32 out: softmax over the k chosen logits
+ * 1 <= k <= min(E, 32).  Logits must be finite (NaN/Inf order is undefined). */
+moe_status moe_route(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
+                     const void* router_w, const float* bias, float* logits, int32_t* topk_ids,
+                     float* topk_w, void* stream);
+
+/* The top-k and softmax of moe_route alone, on caller-given fp32 logits
+ * [T, E] (same outputs and rules as moe_route).                             */
+moe_status moe_route_from_logits(const moe_desc* desc, int32_t T, int32_t k, const float* logits,
+                                 int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Deterministic expert-major route plan ("Dedicated prefill lane", step 1).
+ *   topk_ids  [T*k] int32, flat index f = t*k + s, values in [0, E)
+ *   offsets   [E+1] int32 out: offsets[e] = #{f : ids[f] < e}; offsets[E] = T*k
+ *   perm      [T*k] int32 out: the f of expert e, ascending, at
+ *             perm[offsets[e] .. offsets[e+1])
+ *   inv_perm  [T*k] int32 out: inv_perm[perm[p]] = p
+ *   workspace scratch of >= moe_workspace_bytes(desc, T, k); this call also
+ *             leaves in it the row-tile plan that moe_grouped_ffn reads, so
+ *             pass the same workspace, unchanged, to the moe_grouped_ffn call
+ *             that consumes this plan.                                      */
+moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const int32_t* topk_ids,
+                       int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Expert-grouped SwiGLU ("Dedicated prefill lane", steps 2-4).  For each
+ * expert e and each p in [offsets[e], offsets[e+1]), with f = perm[p],
+ * t = f / k and weight w = topk_w[f]:
+ *   h = w * silu(Wg_e x_t) (.) (Wu_e x_t)        (router weight folded in)
+ *   out_assign[p] = Wd_e h                       fp32, one row per assignment
+ * and for the shared expert (n_shared == 1), every token t:
+ *   shared_out[t] = Wd_s (silu(Wg_s x_t) (.) (Wu_s x_t))   fp32
+ *   hidden      [T, d] act dtype
+ *   topk_w      [T*k] fp32 (from moe_route)
+ *   offsets, perm        from moe_permute
+ *   routed_blob, shared_blob  device copies of moe_pack_experts blobs
+ *             (shared_blob NULL iff n_shared == 0)
+ *   out_assign  [T*k, d] fp32 out, in permuted order (row p)
+ *   shared_out  [T, d] fp32 out (NULL iff n_shared == 0)
+ *   workspace   the workspace moe_permute filled (holds its tile plan and the
+ *               intermediate h).
+ * Arithmetic: bf16 paths multiply on bf16 MFMA with fp32 accumulation; int4
+ * and int8 weights are dequantized to bf16 in registers (int8 exactly, its row
+ * scale applied to the fp32 accumulator); h is stored as bf16.  The fp32 path
+ * computes in fp32 throughout.                                               */
+moe_status moe_grouped_ffn(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
+                           const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                           const void* routed_blob, const void* shared_blob, float* out_assign,
+                           float* shared_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Fixed-order combine ("Dedicated prefill lane", step 5), no atomics:
+ *   y[t] = act( ((out_assign[inv_perm[t*k+0]] + ... ) + out_assign[inv_perm[t*k+k-1]])
+ *               + shared_out[t] )
+ * summed in fp32 in exactly that order, then rounded to the act dtype (bf16:
+ * round to nearest even).  shared_out may be NULL (n_shared == 0).
+ *   y [T, d] act dtype out.                                                 */
+moe_status moe_combine(const moe_desc* desc, int32_t T, int32_t k, const float* out_assign,
+                       const int32_t* inv_perm, const float* shared_out, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,125 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the four
+C-ABI calls on the GPU, and compare against the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import expert_grouped_quantized_amd as M
+import oracle
+import workloads as W
+from expert_grouped_quantized_amd.layer import MoELayer, blobs_from_inputs
+
+ORC_FMT = {W.F32: oracle.F32, W.BF16: oracle.BF16, W.I4G32: oracle.I4G32, W.I8ROW: oracle.I8ROW}
+
+
+def desc_of(cfg: W.LayerConfig):
+    return M.make_desc(cfg.d, cfg.E, cfg.F, cfg.n_shared, cfg.Fs, act=cfg.act,
+                       expert_w=cfg.expert, shared_w=cfg.shared if cfg.n_shared else cfg.act)
+
+
+def spec_of(cfg: W.LayerConfig) -> dict:
+    return dict(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, n_shared=cfg.n_shared, Fs=cfg.Fs,
+                x_fmt=ORC_FMT[cfg.act], expert_fmt=ORC_FMT[cfg.expert],
+                shared_fmt=ORC_FMT[cfg.shared] if cfg.n_shared else 0)
+
+
+class GpuLayer:
+    """Uploads one layer's weights once; runs it on any hidden input."""
+
+    def __init__(self, cfg: W.LayerConfig, inputs: dict, T_max: int | None = None):
+        import torch
+        self.torch, self.cfg, self.inputs = torch, cfg, inputs
+        self.desc = desc_of(cfg)
+        T_max = T_max or inputs["x"].shape[0]
+        self.layer = MoELayer(self.desc, cfg.k, T_max)
+        routed, shared = blobs_from_inputs(self.desc, inputs)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        wr = inputs["wr"]
+        wr_t = dev(wr.view(np.int16)).view(torch.bfloat16) if cfg.act == W.BF16 else dev(wr)
+        bias = None if inputs.get("bias") is None else dev(inputs["bias"])
+        self.layer.set_weights(wr_t, dev(routed), None if shared is None else dev(shared), bias)
+
+    def x_tensor(self, x):
+        t = self.torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
+        return t.view(self.torch.bfloat16) if self.cfg.act == W.BF16 else t
+
+    def run(self, x) -> dict:
+        torch = self.torch
+        T = x.shape[0]
+        L = self.layer
+        y = L.forward(self.x_tensor(x), T)
+        torch.cuda.synchronize()
+        n = T * self.cfg.k
+        cpu = lambda t: t.cpu().numpy()
+        out = dict(logits=cpu(L.logits[:T]), ids=cpu(L.ids[:n]).reshape(T, self.cfg.k),
+                   w=cpu(L.w[:n]).reshape(T, self.cfg.k), offsets=cpu(L.offsets),
+                   perm=cpu(L.perm[:n]), inv_perm=cpu(L.inv_perm[:n]),
+                   out_assign=cpu(L.out_assign[:n]),
+                   shared_out=cpu(L.shared_out[:T]) if self.cfg.n_shared else None)
+        if self.cfg.act == W.BF16:
+            out["y"] = y.float().cpu().numpy()
+            out["y_bits"] = y.view(torch.int16).cpu().numpy()
+        else:
+            out["y"] = cpu(y)
+            out["y_bits"] = y.view(torch.int32).cpu().numpy()
+        return out
+
+
+def rel_l2(a, ref):
+    a, ref = np.asarray(a, np.float64), np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(a - ref) / (den if den > 0 else 1.0)
+
+
+def assert_close(a, ref, fp32: bool, what: str):
+    """bf16/int paths: rel-L2 <= 5e-3 and max|a-ref| <= 2e-2 max|ref|;
+    fp32 path: rel-L2 <= 1e-5."""
+    r = rel_l2(a, ref)
+    if fp32:
+        assert r <= 1e-5, f"{what}: rel-L2 {r:.3e} > 1e-5"
+    else:
+        mx = np.max(np.abs(np.asarray(a, np.float64) - ref))
+        lim = 2e-2 * np.max(np.abs(ref))
+        assert r <= 5e-3, f"{what}: rel-L2 {r:.3e} > 5e-3"
+        assert mx <= lim, f"{what}: max abs err {mx:.3e} > {lim:.3e}"
+    return r
+
+
+def check_route(cfg, inputs, out, tokens=None):
+    """ids bit-exact and w close against the oracle fed the GPU's fp32 logits;
+    GPU logits close to the oracle's own fp64 logits."""
+    T = out["ids"].shape[0]
+    L64 = out["logits"].astype(np.float64)
+    ids_o, w_o = oracle.topk_softmax(L64, cfg.k)
+    assert np.array_equal(out["ids"], ids_o), "top-k ids differ from the oracle"
+    np.testing.assert_allclose(out["w"], w_o, rtol=2e-6, atol=1e-7)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    lo = oracle.router_logits(inputs["x"], ORC_FMT[cfg.act], inputs["wr"], ORC_FMT[cfg.act],
+                              cfg.d, cfg.E, bias=inputs.get("bias"), tokens=tok)
+    err = np.max(np.abs(out["logits"][tok].astype(np.float64) - lo))
+    assert err <= 2e-4 * max(1.0, np.max(np.abs(lo))), f"router logits max err {err:.3e}"
+    return ids_o, w_o
+
+
+def check_plan(cfg, out):
+    off, perm, inv = oracle.route_plan(out["ids"].reshape(-1), cfg.E)
+    assert np.array_equal(out["offsets"], off), "offsets differ"
+    assert np.array_equal(out["perm"], perm), "perm differs"
+    assert np.array_equal(out["inv_perm"], inv), "inv_perm differs"
+
+
+def check_values(cfg, inputs, out, w_o, tokens=None):
+    """y, out_assign and shared_out of the chosen tokens against the oracle."""
+    T = out["ids"].shape[0]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    fp32 = cfg.act == W.F32
+    y_ref, oa_ref, so_ref = oracle.moe_experts(spec_of(cfg), inputs, out["ids"][tok], w_o[tok],
+                                               tokens=tok)
+    r_y = assert_close(out["y"][tok], y_ref, fp32, "y")
+    flat = (tok[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
+    gpu_oa = out["out_assign"][out["inv_perm"][flat]]
+    r_oa = assert_close(gpu_oa, oa_ref, fp32, "out_assign")
+    r_so = None
+    if cfg.n_shared:
+        r_so = assert_close(out["shared_out"][tok], so_ref, fp32, "shared_out")
+    return dict(y=r_y, out_assign=r_oa, shared_out=r_so)
