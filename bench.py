@@ -37,7 +37,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=24)
+    p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    p.add_argument("--workload", choices=("both", "prefill", "decode"), default="both",
+                   help="limit the run to one workload (for per-workload profiles)")
     return p.parse_args()
 
 
@@ -123,13 +125,12 @@ def algorithmic(cfg, T, n_active):
                 layer_bytes=weight_bytes + act + inter)
 
 
-def cpu_baseline(S: Setup, n_tok: int):
+def cpu_baseline(cfg, inp: dict, T: int, n_tok: int):
     """The fp64 oracle (never tuned) on a bounded token sample of the same workload."""
     import oracle
-    cfg, inp = S.cfg, S.inputs
     fm = {"f32": oracle.F32, "bf16": oracle.BF16, "i4g32": oracle.I4G32, "i8row": oracle.I8ROW}
     rng = np.random.default_rng(123)
-    tok = np.sort(rng.choice(S.T, size=min(n_tok, S.T), replace=False))
+    tok = np.sort(rng.choice(T, size=min(n_tok, T), replace=False))
     spec = dict(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, n_shared=cfg.n_shared, Fs=cfg.Fs,
                 x_fmt=fm[cfg.act], expert_fmt=fm[cfg.expert], shared_fmt=fm[cfg.shared])
     t0 = time.perf_counter()
@@ -140,8 +141,64 @@ def cpu_baseline(S: Setup, n_tok: int):
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(len(tok) / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(tok)} of the {S.T} tokens of the same seeded workload, whole layer "
+            "sample": f"{len(tok)} of the {T} tokens of the same seeded workload, whole layer "
                       f"(fp64 router, top-k, per-expert SwiGLU, shared expert, sum); {dt:.1f} s"}
+
+
+def run_prefill(args, torch, W):
+    """The T=4096 prefill workload; returns (result dict, roofline dict, host inputs)."""
+    cfg = W.CONFIGS["int4_T4096"]
+    S = Setup(cfg, cfg.T, torch)
+    wall, layer_ms, per_call = time_steps(S, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    n_active = int((np.diff(S.layer.offsets.cpu().numpy()) > 0).sum())
+    A = algorithmic(cfg, cfg.T, n_active)
+    ffn_ms = per_call[2]
+    ffn_tflops = A["ffn_flops"] / (ffn_ms * 1e-3) / 1e12
+    layer_tflops = (A["ffn_flops"] + A["router_flops"]) / (ms_per_step * 1e-3) / 1e12
+    res = dict(T=cfg.T, tokens_per_s=cfg.T / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
+               layer_event_ms=layer_ms,
+               call_ms=dict(route=per_call[0], permute=per_call[1], grouped_ffn=per_call[2],
+                            combine=per_call[3]),
+               layer_tflops=layer_tflops, layer_mfma_frac=layer_tflops / BF16_PEAK_TFLOPS,
+               layer_gbs=A["layer_bytes"] / (ms_per_step * 1e-3) / 1e9)
+    roof = {"bound": "mfma", "kernel": "moe_grouped_ffn (gate/up + down GEMMs)",
+            "achieved": round(ffn_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ffn_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": A["ffn_flops"], "avg_launch_ms": round(ffn_ms, 4)}
+    inputs = S.inputs
+    del S
+    torch.cuda.empty_cache()
+    return res, roof, inputs
+
+
+def run_decode(args, torch, W):
+    """The T=16 decode / verify workload; returns (result dict, roofline dict)."""
+    dcfg = W.CONFIGS["int4_decode"]
+    D = Setup(dcfg, 16, torch)
+    dwall, dlayer_ms, dper = time_steps(D, args.decode_steps, 10)
+    d_ms = dwall * 1e3 / args.decode_steps
+    d_active = int((np.diff(D.layer.offsets.cpu().numpy()) > 0).sum())
+    DA = algorithmic(dcfg, 16, d_active)
+    ffn_gbs = DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9
+    res = dict(T=16, tokens_per_s=16 / (d_ms * 1e-3), ms_per_step=d_ms, active_experts=d_active,
+               layer_event_ms=dlayer_ms,
+               call_ms=dict(route=dper[0], permute=dper[1], grouped_ffn=dper[2], combine=dper[3]),
+               weight_bytes=DA["weight_bytes"],
+               layer_hbm_frac=DA["layer_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               ffn_weight_gbs=ffn_gbs)
+    roof = {"bound": "hbm", "kernel": "moe_grouped_ffn (gate/up + down weight streams)",
+            "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": DA["weight_bytes"], "avg_launch_ms": round(dper[2], 4)}
+    del D
+    torch.cuda.empty_cache()
+    return res, roof
+
+
+def _r(d):
+    return {k: (round(v, 4) if isinstance(v, float) else _r(v) if isinstance(v, dict) else v)
+            for k, v in d.items()}
 
 
 def main():
@@ -155,70 +212,52 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    # ---- headline: T=4096 prefill
-    cfg = W.CONFIGS["int4_T4096"]
-    S = Setup(cfg, cfg.T, torch)
-    wall, layer_ms, per_call = time_steps(S, args.steps, args.warmup)
-    ms_per_step = wall * 1e3 / args.steps
-    n_active = int((np.diff(S.layer.offsets.cpu().numpy()) > 0).sum())
-    A = algorithmic(cfg, cfg.T, n_active)
-    ffn_ms = per_call[2]
-    ffn_tflops = A["ffn_flops"] / (ffn_ms * 1e-3) / 1e12
-    layer_tflops = (A["ffn_flops"] + A["router_flops"]) / (ms_per_step * 1e-3) / 1e12
-    prefill = dict(tokens_per_s=cfg.T / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
-                   layer_event_ms=layer_ms,
-                   call_ms=dict(route=per_call[0], permute=per_call[1], grouped_ffn=per_call[2],
-                                combine=per_call[3]),
-                   layer_tflops=layer_tflops, layer_mfma_frac=layer_tflops / BF16_PEAK_TFLOPS,
-                   layer_gbs=A["layer_bytes"] / (ms_per_step * 1e-3) / 1e9)
-    del S
-    torch.cuda.empty_cache()
-
-    # ---- decode / verify batch, T=16
-    dcfg = W.CONFIGS["int4_decode"]
-    D = Setup(dcfg, 16, torch)
-    dwall, dlayer_ms, dper = time_steps(D, args.decode_steps, 10)
-    d_ms = dwall * 1e3 / args.decode_steps
-    d_active = int((np.diff(D.layer.offsets.cpu().numpy()) > 0).sum())
-    DA = algorithmic(dcfg, 16, d_active)
-    decode = dict(T=16, tokens_per_s=16 / (d_ms * 1e-3), ms_per_step=d_ms, active_experts=d_active,
-                  layer_event_ms=dlayer_ms,
-                  call_ms=dict(route=dper[0], permute=dper[1], grouped_ffn=dper[2], combine=dper[3]),
-                  weight_bytes=DA["weight_bytes"],
-                  layer_hbm_frac=DA["layer_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                  ffn_weight_gbs=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9)
-
+    prefill = decode = roof_p = roof_d = pre_inputs = None
+    if args.workload in ("both", "prefill"):
+        prefill, roof_p, pre_inputs = run_prefill(args, torch, W)
+    if args.workload in ("both", "decode"):
+        decode, roof_d = run_decode(args, torch, W)
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(D if False else Setup(cfg, cfg.T, torch), args.cpu_sample_tokens)
+    if not args.no_cpu_baseline and pre_inputs is not None:
+        cfg = W.CONFIGS["int4_T4096"]
+        cpu = cpu_baseline(cfg, pre_inputs, cfg.T, args.cpu_sample_tokens)
 
+    cfg = W.CONFIGS["int4_T4096"]
+    common = {"d": cfg.d, "E": cfg.E, "k": cfg.k, "n_shared": cfg.n_shared, "F": cfg.F,
+              "routed_w": "int4 g32 fp16 scales", "shared_w": "int8 per-row fp16 scales",
+              "activations": "bf16"}
+    if prefill is not None:
+        head, roof, steps = prefill, roof_p, args.steps
+        metric = "MoE-layer tokens/s at T=4096 prefill (int4 g32 experts, int8 shared)"
+        workload = "moe_layer_int4_T4096_prefill"
+        warm = args.warmup
+    else:
+        head, roof, steps = decode, roof_d, args.decode_steps
+        metric = "MoE-layer tokens/s at T=16 decode (int4 g32 experts, int8 shared)"
+        workload = "moe_layer_int4_T16_decode"
+        warm = 10
     line = {
-        "metric": "MoE-layer tokens/s at T=4096 prefill (int4 g32 experts, int8 shared)",
-        "value": round(prefill["tokens_per_s"], 1),
+        "metric": metric,
+        "value": round(head["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "moe_layer_int4_T4096_prefill", "T": cfg.T, "d": cfg.d,
-                   "E": cfg.E, "k": cfg.k, "n_shared": cfg.n_shared, "F": cfg.F,
-                   "routed_w": "int4 g32 fp16 scales", "shared_w": "int8 per-row fp16 scales",
-                   "activations": "bf16"},
-        "roofline": {"bound": "mfma", "kernel": "moe_grouped_ffn (gate/up + down GEMMs)",
-                     "achieved": round(ffn_tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ffn_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None,
-                     "algorithmic_flops_per_launch": A["ffn_flops"],
-                     "avg_launch_ms": round(ffn_ms, 4)},
+        "config": dict({"workload": workload, "T": head["T"]}, **common),
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
-        "decode": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in decode.items()},
     }
+    if prefill is not None:
+        line["prefill"] = _r(prefill)
+    if decode is not None:
+        line["decode"] = _r(decode)
+        line["decode_roofline"] = roof_d
     print(json.dumps(line, default=float), flush=True)
 
 

@@ -109,65 +109,71 @@ inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
   return ((const uint16_t*)m.s)[r * (m.K / 32) + k / 32];
 }
 
-// One 64-row x 64-K wave tile.  Fragment f (0 or 1) takes its 32 rows from
-// matrix m[f], rows row_of(f, c) for c = 0..31; lane l of the consuming wave
-// holds row c = l % 32, K offsets 8*(l/32) .. +7 of each 16-wide K step.
+// One 64-row x 64-K wave tile, laid out for the 16x16x32 MFMA.  Fragment f
+// (0..3) takes 16 rows from matrix m[f], rows row_of(f, c) for c = 0..15;
+// K step s (0..1) covers 32 K.  Lane l of the consuming wave holds row
+// c = l % 16 and K offsets 32*s + 8*(l/16) .. +7.
+//   BF16: 16-byte piece (f*2 + s, lane) at ((f*2 + s)*64 + lane)*16
+//   I4  : dword (code + 8 per nibble, element i in nibble i) at
+//         ((f/2)*64 + lane)*16 + ((f%2)*2 + s)*4; then per row c the 8 fp16
+//         group scales [f][s] at 2048 + c*16
+//   I8  : 8 bytes (code + 128) at (f*64 + lane)*16 + s*8
 struct OutIO {  // canonical outputs of unpacking
   uint8_t* q;
   uint8_t* s;
 };
 
 template <typename RowOf>
-bool pack_tile(const MatIO* const m[2], RowOf row_of, int64_t kc, uint8_t* dst) {
+bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   const int fmt = m[0]->fmt;
-  for (int f = 0; f < 2; f++) {
+  for (int f = 0; f < 4; f++) {
     const MatIO& M = *m[f];
     for (int lane = 0; lane < 64; lane++) {
-      const int64_t r = row_of(f, lane & 31);
-      for (int s = 0; s < 4; s++) {
-        const int64_t k0 = kc * KC + s * 16 + 8 * (lane >> 5);
+      const int64_t r = row_of(f, lane & 15);
+      for (int s = 0; s < 2; s++) {
+        const int64_t k0 = kc * KC + s * 32 + 8 * (lane >> 4);
         if (fmt == MOE_BF16) {
-          memcpy(dst + ((size_t)(f * 4 + s) * 64 + lane) * 16, (const uint16_t*)M.q + r * M.K + k0, 16);
+          memcpy(dst + ((size_t)(f * 2 + s) * 64 + lane) * 16, (const uint16_t*)M.q + r * M.K + k0, 16);
         } else if (fmt == MOE_I4_G32) {
-          uint32_t word = 0;  // nibble i = code of element k0 + i, stored as code + 8
+          uint32_t word = 0;
           for (int i = 0; i < 8; i++) {
             const int c = i4_code(M, r, k0 + i);
             if (c < -7) return false;
             word |= (uint32_t)(c + 8) << (4 * i);
           }
-          memcpy(dst + ((size_t)f * 64 + lane) * 16 + s * 4, &word, 4);
-        } else {  // I8: byte i = code + 128
-          uint8_t* o = dst + ((size_t)(f * 2 + (s >> 1)) * 64 + lane) * 16 + (s & 1) * 8;
+          memcpy(dst + ((size_t)(f >> 1) * 64 + lane) * 16 + ((f & 1) * 2 + s) * 4, &word, 4);
+        } else {  // I8
+          uint8_t* o = dst + ((size_t)f * 64 + lane) * 16 + s * 8;
           for (int i = 0; i < 8; i++) o[i] = (uint8_t)((int)((const int8_t*)M.q)[r * M.K + k0 + i] + 128);
         }
       }
     }
   }
-  if (fmt == MOE_I4_G32) {  // per row c: [frag0 group0, frag0 group1, frag1 group0, frag1 group1]
-    for (int c = 0; c < 32; c++) {
-      uint16_t* o = (uint16_t*)(dst + 2048 + c * 8);
-      for (int f = 0; f < 2; f++)
-        for (int g = 0; g < 2; g++) o[f * 2 + g] = i4_scale(*m[f], row_of(f, c), kc * KC + g * 32);
+  if (fmt == MOE_I4_G32) {
+    for (int c = 0; c < 16; c++) {
+      uint16_t* o = (uint16_t*)(dst + 2048 + c * 16);
+      for (int f = 0; f < 4; f++)
+        for (int s = 0; s < 2; s++) o[f * 2 + s] = i4_scale(*m[f], row_of(f, c), kc * KC + s * 32);
     }
   }
   return true;
 }
 
 template <typename RowOf>
-void unpack_tile(const MatIO* const m[2], const OutIO out[2], RowOf row_of, int64_t kc,
+void unpack_tile(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int64_t kc,
                  const uint8_t* src) {
   const int fmt = m[0]->fmt;
-  for (int f = 0; f < 2; f++) {
+  for (int f = 0; f < 4; f++) {
     const int64_t K = m[f]->K;
     for (int lane = 0; lane < 64; lane++) {
-      const int64_t r = row_of(f, lane & 31);
-      for (int s = 0; s < 4; s++) {
-        const int64_t k0 = kc * KC + s * 16 + 8 * (lane >> 5);
+      const int64_t r = row_of(f, lane & 15);
+      for (int s = 0; s < 2; s++) {
+        const int64_t k0 = kc * KC + s * 32 + 8 * (lane >> 4);
         if (fmt == MOE_BF16) {
-          memcpy((uint16_t*)out[f].q + r * K + k0, src + ((size_t)(f * 4 + s) * 64 + lane) * 16, 16);
+          memcpy((uint16_t*)out[f].q + r * K + k0, src + ((size_t)(f * 2 + s) * 64 + lane) * 16, 16);
         } else if (fmt == MOE_I4_G32) {
           uint32_t word;
-          memcpy(&word, src + ((size_t)f * 64 + lane) * 16 + s * 4, 4);
+          memcpy(&word, src + ((size_t)(f >> 1) * 64 + lane) * 16 + ((f & 1) * 2 + s) * 4, 4);
           for (int i = 0; i < 8; i++) {
             const int c = (int)((word >> (4 * i)) & 15) - 8;
             const int64_t k = k0 + i;
@@ -176,18 +182,18 @@ void unpack_tile(const MatIO* const m[2], const OutIO out[2], RowOf row_of, int6
             b = (k & 1) ? (uint8_t)((b & 0x0f) | (nib << 4)) : (uint8_t)((b & 0xf0) | nib);
           }
         } else {
-          const uint8_t* o = src + ((size_t)(f * 2 + (s >> 1)) * 64 + lane) * 16 + (s & 1) * 8;
+          const uint8_t* o = src + ((size_t)f * 64 + lane) * 16 + s * 8;
           for (int i = 0; i < 8; i++) ((int8_t*)out[f].q)[r * K + k0 + i] = (int8_t)((int)o[i] - 128);
         }
       }
     }
   }
   if (fmt == MOE_I4_G32) {
-    for (int c = 0; c < 32; c++) {
-      const uint16_t* o = (const uint16_t*)(src + 2048 + c * 8);
-      for (int f = 0; f < 2; f++)
-        for (int g = 0; g < 2; g++)
-          ((uint16_t*)out[f].s)[row_of(f, c) * (m[f]->K / 32) + 2 * kc + g] = o[f * 2 + g];
+    for (int c = 0; c < 16; c++) {
+      const uint16_t* o = (const uint16_t*)(src + 2048 + c * 16);
+      for (int f = 0; f < 4; f++)
+        for (int s = 0; s < 2; s++)
+          ((uint16_t*)out[f].s)[row_of(f, c) * (m[f]->K / 32) + 2 * kc + s] = o[f * 2 + s];
     }
   }
 }
@@ -226,13 +232,15 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
   const size_t tb = tile_bytes(fmt);
   const int64_t nk1 = d / KC, nk2 = F / KC;
   const MatIO G{fmt, F, d, io.g, io.gs}, U{fmt, F, d, io.u, io.us}, Dn{fmt, d, F, io.dn, io.ds};
-  // W1 wave tile (nb, w): frag 0 = gate rows, frag 1 = up rows nb*128 + w*32 + c
-  const MatIO* const m1[2] = {&G, &U};
-  const OutIO o1[2] = {{(uint8_t*)io.g, (uint8_t*)io.gs}, {(uint8_t*)io.u, (uint8_t*)io.us}};
+  // W1 wave tile (nb, w), h columns c0 = nb*128 + w*32: fragments 0, 1 = gate
+  // rows c0 + 16*(f%2) + c, fragments 2, 3 = up rows of the same columns
+  const MatIO* const m1[4] = {&G, &G, &U, &U};
+  const OutIO og{(uint8_t*)io.g, (uint8_t*)io.gs}, ou{(uint8_t*)io.u, (uint8_t*)io.us};
+  const OutIO o1[4] = {og, og, ou, ou};
   for (int64_t nb = 0; nb < F / H_COLS_BLOCK; nb++) {
     for (int w = 0; w < WAVES; w++) {
-      const int64_t rbase = nb * H_COLS_BLOCK + w * 32;
-      auto row_of = [rbase](int, int c) { return rbase + c; };
+      const int64_t c0 = nb * H_COLS_BLOCK + w * 32;
+      auto row_of = [c0](int f, int c) { return c0 + (f & 1) * 16 + c; };
       for (int64_t kc = 0; kc < nk1; kc++) {
         uint8_t* t = blob + ((size_t)(nb * WAVES + w) * nk1 + kc) * tb;
         if (!unpack) {
@@ -243,14 +251,15 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
       }
     }
   }
-  // W2 wave tile (nb, w): frag f = down rows nb*256 + w*64 + f*32 + c
+  // W2 wave tile (nb, w): fragment f = down rows nb*256 + w*64 + 16*f + c
   uint8_t* w2 = blob + w1b;
-  const MatIO* const m2[2] = {&Dn, &Dn};
-  const OutIO o2[2] = {{(uint8_t*)io.dn, (uint8_t*)io.ds}, {(uint8_t*)io.dn, (uint8_t*)io.ds}};
+  const MatIO* const m2[4] = {&Dn, &Dn, &Dn, &Dn};
+  const OutIO od{(uint8_t*)io.dn, (uint8_t*)io.ds};
+  const OutIO o2[4] = {od, od, od, od};
   for (int64_t nb = 0; nb < d / OUT_COLS_BLOCK; nb++) {
     for (int w = 0; w < WAVES; w++) {
       const int64_t rbase = nb * OUT_COLS_BLOCK + w * 64;
-      auto row_of = [rbase](int f, int c) { return rbase + f * 32 + c; };
+      auto row_of = [rbase](int f, int c) { return rbase + f * 16 + c; };
       for (int64_t kc = 0; kc < nk2; kc++) {
         uint8_t* t = w2 + ((size_t)(nb * WAVES + w) * nk2 + kc) * tb;
         if (!unpack) {

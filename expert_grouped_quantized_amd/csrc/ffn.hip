@@ -1,8 +1,8 @@
 // ffn.hip -- expert-grouped SwiGLU GEMMs ("Qwen3.8-Flash-Next-Dual-GPU"
 // README, section "Dedicated prefill lane", steps 2-4).
 //
-// Work unit: one row tile (up to BM = 128 consecutive rows of one expert's
-// group in the route plan, or 128 tokens of the always-active shared expert)
+// Work unit: one row tile (up to BM = 96 consecutive rows of one expert's group
+// in the route plan, or up to 96 tokens of the always-active shared expert)
 // times one column block.  A block is 4 wave64s:
 //   stage 1: h[p] = w_p * silu(Wg x_t) (.) (Wu x_t)   -> h (bf16), rows p
 //            each wave owns 32 h columns: 32 gate rows and 32 up rows of W1
@@ -12,19 +12,27 @@
 // Activations (x rows gathered through perm, or h rows) are staged through
 // LDS, 64 K at a time, double-buffered, and read as MFMA A operands by all 4
 // waves.  Weights stream straight from HBM into each wave's registers in the
-// tile order moe_pack_experts wrote them (one contiguous run per wave), are
-// dequantized in registers to bf16 (int4: code * fp16 group scale, rounded to
-// nearest even; int8: the exact code, its row scale applied to the fp32
-// accumulator), and feed bf16 MFMA 32x32x16 with fp32 accumulation.  A wave
-// covers all rows of its tile, so each weight is read and dequantized once per
-// row tile.  Row tiles with fewer than 128 rows skip their empty 32-row MFMA
-// fragments.
+// tile order moe_pack_experts wrote them (one contiguous run per wave), PF
+// chunks ahead, are dequantized in registers to bf16 (int4: code * fp16 group
+// scale, rounded to nearest even; int8: the exact code, its row scale applied
+// to the fp32 accumulator), and feed bf16 MFMA 16x16x32 with fp32
+// accumulation.  A wave covers all rows of its tile, so each weight is read
+// and dequantized once per row tile; 16-row MFMA fragments past the tile's
+// last row are skipped.
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
+typedef __bf16 bf16x8_f __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4_t mfma16x16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_f, a),
+                                                 __builtin_bit_cast(bf16x8_f, b), c, 0, 0, 0);
+}
+
 // ---- weight registers of one wave tile (64 rows x 64 K) -------------------
+// Fragment f (0..3) is 16 weight rows; step s (0..1) is 32 K.  Lane l holds
+// row l % 16 of each fragment and K elements 32*s + 8*(l/16) .. +7.
 template <int FMT>
 struct WTile;
 
@@ -35,23 +43,24 @@ struct WTile<MOE_BF16> {
 #pragma unroll
     for (int j = 0; j < 8; j++) v[j] = ((const u32x4_t*)t)[j * 64 + lane];
   }
-  __device__ __forceinline__ u32x4_t frag(int f, int s) const { return v[f * 4 + s]; }
+  __device__ __forceinline__ u32x4_t frag(int f, int s) const { return v[f * 2 + s]; }
 };
 
 template <>
 struct WTile<MOE_I4_G32> {
-  u32x4_t v[2];  // [frag], component = step; nibbles hold code + 8
-  uint2 sc;      // fp16 scales: frag0 group0, frag0 group1, frag1 group0, frag1 group1
+  u32x4_t v[2];  // [frag pair]; dword (f%2)*2 + s holds 8 nibbles = code + 8
+  u32x4_t sc;    // 8 fp16 group scales, index f*2 + s (group = step)
   __device__ __forceinline__ void load(const uint8_t* t, int lane) {
     v[0] = ((const u32x4_t*)t)[lane];
     v[1] = ((const u32x4_t*)t)[64 + lane];
-    sc = ((const uint2*)(t + 2048))[lane & 31];
+    sc = ((const u32x4_t*)(t + 2048))[lane & 15];
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s) const {
-    const uint32_t word = f ? (s < 2 ? sc.y & 0xffffu : sc.y >> 16) : (s < 2 ? sc.x & 0xffffu : sc.x >> 16);
-    const float scale = f16_bits_to_f32((uint16_t)word);
+    const int si = f * 2 + s;
+    const uint32_t sw = sc[si >> 1];
+    const float scale = f16_bits_to_f32((uint16_t)((si & 1) ? (sw >> 16) : (sw & 0xffffu)));
     const float bias = -8.0f * scale;
-    const uint32_t q = v[f][s];
+    const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
     const uint32_t lo = q & 0x0f0f0f0fu, hi = (q >> 4) & 0x0f0f0f0fu;
     u32x4_t r;
     r[0] = pack_bf16x2(fmaf((float)(lo & 0xff), scale, bias), fmaf((float)(hi & 0xff), scale, bias));
@@ -66,14 +75,13 @@ struct WTile<MOE_I4_G32> {
 
 template <>
 struct WTile<MOE_I8_ROW> {
-  u32x4_t v[4];  // [frag][half]; bytes hold code + 128
+  u32x4_t v[4];  // [frag]; dwords 2s, 2s+1 hold 8 bytes = code + 128
   __device__ __forceinline__ void load(const uint8_t* t, int lane) {
 #pragma unroll
     for (int j = 0; j < 4; j++) v[j] = ((const u32x4_t*)t)[j * 64 + lane];
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s) const {
-    const u32x4_t& h = v[f * 2 + (s >> 1)];
-    const uint32_t w0 = h[(s & 1) * 2], w1 = h[(s & 1) * 2 + 1];
+    const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
     u32x4_t r;
     r[0] = pack_bf16x2((float)(w0 & 0xff) - 128.0f, (float)((w0 >> 8) & 0xff) - 128.0f);
     r[1] = pack_bf16x2((float)((w0 >> 16) & 0xff) - 128.0f, (float)(w0 >> 24) - 128.0f);
@@ -89,28 +97,167 @@ struct TileJob {
   int expert, start, cnt, nb;
 };
 
+template <int MAXMF>
 struct Smem {
-  uint16_t a[2][BM * 64];
-  float wrow[BM];
-  int src[BM];
+  uint16_t a[2][MAXMF * 16 * 64];
+  float wrow[MAXMF * 16];
+  int src[MAXMF * 16];
 };
 
-template <int FMT, int STAGE>
-__device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Smem& sm) {
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Per-tile constants shared by the setup and the main loop.
+struct TileCtx {
+  int Fw, nk;
+  const uint8_t* sect;  // W1 or W2 section of this expert's blob
+  const uint8_t* wt;    // this wave's run of weight tiles
+  const uint16_t* arow[3];
+  bool a_loader;
+};
+
+template <int FMT, int STAGE, int MAXMF, int PF_MAX, int NMF>
+__device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm,
+                                          const TileCtx& C) {
+  // a bf16 wave tile is 4x the bytes (and registers) of an int4 one
+  constexpr int PF = FMT == MOE_BF16 ? 2 : PF_MAX;
+  constexpr int ROWS = MAXMF * 16;
+  constexpr int PIECES = ROWS * 8;
+  constexpr int PPT = PIECES >= 256 ? PIECES / 256 : 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Fw = J.shared ? A.Fs : A.F;
-  const int K = STAGE == 1 ? A.d : Fw;
-  const int nk = K / KC;
+  const int nk = C.nk;
+  const size_t tb = tile_bytes(FMT);
+  const int c8 = tid & 7;
+
+  f32x4_t acc[NMF][4];
+#pragma unroll
+  for (int i = 0; i < NMF; i++)
+#pragma unroll
+    for (int f = 0; f < 4; f++) acc[i][f] = f32x4_t{0, 0, 0, 0};
+
+  // A chunks are prefetched two ahead: chunk c travels in register set c & 1,
+  // then lands in LDS buffer c & 1.  Weight chunks are prefetched PF ahead in a
+  // ring of registers.  PF is even, so every index below is a compile-time one.
+  u32x4_t areg[2][PPT];
+  auto load_a = [&](int kc, u32x4_t (&dst)[PPT]) {
+#pragma unroll
+    for (int j = 0; j < PPT; j++)
+      dst[j] = C.arow[j] ? *(const u32x4_t*)(C.arow[j] + kc * KC) : u32x4_t{0, 0, 0, 0};
+  };
+  auto store_a = [&](uint16_t* dst, const u32x4_t (&src)[PPT]) {
+    if (C.a_loader) {
+#pragma unroll
+      for (int j = 0; j < PPT; j++) *(u32x4_t*)(dst + lds_a_index((tid >> 3) + 32 * j, c8)) = src[j];
+    }
+  };
+  auto compute = [&](const uint16_t* as, const WTile<FMT>& w) {
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const int ch = 4 * s + (lane >> 4);
+      u32x4_t av[NMF];
+#pragma unroll
+      for (int i = 0; i < NMF; i++)
+        av[i] = *(const u32x4_t*)(as + lds_a_index(i * 16 + (lane & 15), ch));
+#pragma unroll
+      for (int f = 0; f < 4; f++) {
+        const u32x4_t b = w.frag(f, s);
+#pragma unroll
+        for (int i = 0; i < NMF; i++) acc[i][f] = mfma16x16(av[i], b, acc[i][f]);
+      }
+    }
+  };
+
+  static_assert(PF % 2 == 0, "weight prefetch depth must be even");
+  WTile<FMT> ring[PF];
+#pragma unroll
+  for (int p = 0; p < PF; p++)
+    if (p < nk) ring[p].load(C.wt + (size_t)p * tb, lane);
+  load_a(0, areg[0]);
+  if (1 < nk) load_a(1, areg[1]);
+  store_a(sm.a[0], areg[0]);
+  __syncthreads();
+  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; p++) {
+      const int kc = kc0 + p;
+      if (kc < nk) {  // block-uniform
+        if (kc + 2 < nk) load_a(kc + 2, areg[p & 1]);
+        compute(sm.a[p & 1], ring[p]);
+        if (kc + PF < nk) ring[p].load(C.wt + (size_t)(kc + PF) * tb, lane);
+        if (kc + 1 < nk) store_a(sm.a[(p + 1) & 1], areg[(p + 1) & 1]);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- epilogue.  Accumulator r of fragment (i, f) is row i*16 + 4*(lane/16)
+  // + r and column 16*f + lane%16 of the wave's 64 weight rows.
+  const int Fw = C.Fw;
+  const uint16_t* rscale =
+      FMT == MOE_I8_ROW
+          ? (const uint16_t*)(C.sect + (size_t)(STAGE == 1 ? (2 * Fw / 64) * (A.d / KC) : (A.d / 64) * (Fw / KC)) * tb)
+          : nullptr;
+  if (STAGE == 1) {
+    uint16_t* hout = (uint16_t*)(J.shared ? A.h_shared : A.h_routed);
+#pragma unroll
+    for (int f = 0; f < 2; f++) {  // fragments 0,1 = gate, 2,3 = up of the same columns
+      const int col = J.nb * H_COLS_BLOCK + wave * 32 + f * 16 + (lane & 15);
+      float sg = 1.0f, su = 1.0f;
+      if (FMT == MOE_I8_ROW) {
+        sg = f16_bits_to_f32(rscale[col]);
+        su = f16_bits_to_f32(rscale[Fw + col]);
+      }
+#pragma unroll
+      for (int i = 0; i < NMF; i++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int m = i * 16 + 4 * (lane >> 4) + r;
+          if (m < J.cnt) {
+            const float g = acc[i][f][r] * sg, u = acc[i][f + 2][r] * su;
+            const float h = sm.wrow[m] * silu_fast(g) * u;
+            hout[(size_t)(J.start + m) * Fw + col] = (uint16_t)(pack_bf16x2(h, 0.0f) & 0xffffu);
+          }
+        }
+      }
+    }
+  } else {
+    float* out = J.shared ? A.shared_out : A.out_assign;
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+      const int col = J.nb * OUT_COLS_BLOCK + wave * 64 + f * 16 + (lane & 15);
+      const float sc = FMT == MOE_I8_ROW ? f16_bits_to_f32(rscale[col]) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < NMF; i++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int m = i * 16 + 4 * (lane >> 4) + r;
+          if (m < J.cnt) out[(size_t)(J.start + m) * A.d + col] = acc[i][f][r] * sc;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int STAGE, int MAXMF, int PF_MAX>
+__device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm) {
+  constexpr int ROWS = MAXMF * 16;
+  constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
+  constexpr int PPT = PIECES >= 256 ? PIECES / 256 : 1;
+  static_assert(PPT <= 3, "A staging holds at most 3 pieces per thread");
+  const int tid = threadIdx.x, wave = tid >> 6;
+  TileCtx C;
+  C.Fw = J.shared ? A.Fs : A.F;
+  const int K = STAGE == 1 ? A.d : C.Fw;
+  C.nk = K / KC;
   const size_t tb = tile_bytes(FMT);
   const uint8_t* blob = J.shared ? A.shared_blob
                                  : A.routed_blob + (size_t)J.expert * expert_bytes(FMT, A.d, A.F);
-  const size_t w1b = w1_bytes(FMT, A.d, Fw);
-  const uint8_t* sect = STAGE == 1 ? blob : blob + w1b;
-  const uint8_t* wt = sect + (size_t)(J.nb * WAVES + wave) * nk * tb;
+  C.sect = STAGE == 1 ? blob : blob + w1_bytes(FMT, A.d, C.Fw);
+  C.wt = C.sect + (size_t)(J.nb * WAVES + wave) * C.nk * tb;
 
   // rows of this tile: source row of the activations and folded router weight
-  if (tid < BM) {
-    const int m = tid;
+  for (int m = tid; m < ROWS; m += 256) {
     int src = -1;
     float wf = 0.0f;
     if (m < J.cnt) {
@@ -134,109 +281,24 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
 
   const uint16_t* abase = STAGE == 1 ? (const uint16_t*)A.hidden
                                      : (const uint16_t*)(J.shared ? A.h_shared : A.h_routed);
-  const size_t astride = STAGE == 1 ? (size_t)A.d : (size_t)Fw;
-  const int c8 = tid & 7;
-  const uint16_t* arow[4];
+  const size_t astride = STAGE == 1 ? (size_t)A.d : (size_t)C.Fw;
+  C.a_loader = tid < PIECES;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int s = sm.src[(tid >> 3) + 32 * j];
-    arow[j] = s >= 0 ? abase + (size_t)s * astride + c8 * 8 : nullptr;
+  for (int j = 0; j < 3; j++) {
+    const int r = (tid >> 3) + 32 * j;
+    const int s = (j < PPT && C.a_loader && r < ROWS) ? sm.src[r] : -1;
+    C.arow[j] = s >= 0 ? abase + (size_t)s * astride + (tid & 7) * 8 : nullptr;
   }
-  const int nmf = (J.cnt + 31) >> 5;  // active 32-row fragments
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; i++) acc[i][0] = acc[i][1] = f32x16_t{};
-
-  u32x4_t areg[4];
-  auto load_a = [&](int kc) {
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-      areg[j] = arow[j] ? *(const u32x4_t*)(arow[j] + kc * KC) : u32x4_t{0, 0, 0, 0};
-  };
-  auto store_a = [&](uint16_t* dst) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) *(u32x4_t*)(dst + lds_a_index((tid >> 3) + 32 * j, c8)) = areg[j];
-  };
-  auto compute = [&](const uint16_t* as, const WTile<FMT>& w) {
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      const u32x4_t b0 = w.frag(0, s), b1 = w.frag(1, s);
-      const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (i < nmf) {
-          const u32x4_t av = *(const u32x4_t*)(as + lds_a_index(i * 32 + (lane & 31), ch));
-          acc[i][0] = mfma32(av, b0, acc[i][0]);
-          acc[i][1] = mfma32(av, b1, acc[i][1]);
-        }
-      }
-    }
-  };
-
-  WTile<FMT> w0, w1;
-  load_a(0);
-  w0.load(wt, lane);
-  store_a(sm.a[0]);
-  __syncthreads();
-  for (int kc = 0; kc < nk; kc += 2) {  // nk is even: K is a multiple of 128
-    load_a(kc + 1);
-    w1.load(wt + (size_t)(kc + 1) * tb, lane);
-    compute(sm.a[0], w0);
-    store_a(sm.a[1]);
-    __syncthreads();
-    if (kc + 2 < nk) {
-      load_a(kc + 2);
-      w0.load(wt + (size_t)(kc + 2) * tb, lane);
-    }
-    compute(sm.a[1], w1);
-    if (kc + 2 < nk) store_a(sm.a[0]);
-    __syncthreads();
-  }
-
-  // ---- epilogue
-  const uint16_t* rscale =
-      FMT == MOE_I8_ROW ? (const uint16_t*)(sect + (size_t)(STAGE == 1 ? (2 * Fw / 64) * (A.d / KC) : (A.d / 64) * (Fw / KC)) * tb)
-                        : nullptr;
-  if (STAGE == 1) {
-    const int col = J.nb * H_COLS_BLOCK + wave * 32 + (lane & 31);
-    float sg = 1.0f, su = 1.0f;
-    if (FMT == MOE_I8_ROW) {
-      sg = f16_bits_to_f32(rscale[col]);
-      su = f16_bits_to_f32(rscale[Fw + col]);
-    }
-    uint16_t* hout = (uint16_t*)(J.shared ? A.h_shared : A.h_routed);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if (i < nmf) {
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < J.cnt) {
-            const float g = acc[i][0][r] * sg, u = acc[i][1][r] * su;
-            const float h = sm.wrow[m] * silu_f(g) * u;
-            hout[(size_t)(J.start + m) * Fw + col] = (uint16_t)(pack_bf16x2(h, 0.0f) & 0xffffu);
-          }
-        }
-      }
-    }
-  } else {
-    float* out = J.shared ? A.shared_out : A.out_assign;
-#pragma unroll
-    for (int f = 0; f < 2; f++) {
-      const int col = J.nb * OUT_COLS_BLOCK + wave * 64 + f * 32 + (lane & 31);
-      const float sc = FMT == MOE_I8_ROW ? f16_bits_to_f32(rscale[col]) : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (i < nmf) {
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int m = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < J.cnt) out[(size_t)(J.start + m) * A.d + col] = acc[i][f][r] * sc;
-          }
-        }
-      }
-    }
+  // the number of live 16-row fragments is a compile-time constant of the
+  // loop, so every step issues its A reads together and runs branch-free
+  const int nmf = (J.cnt + 15) >> 4;
+  switch (nmf) {
+    case 1: tile_body<FMT, STAGE, MAXMF, PF_MAX, 1>(A, J, sm, C); break;
+    case 2: if constexpr (MAXMF >= 2) tile_body<FMT, STAGE, MAXMF, PF_MAX, 2>(A, J, sm, C); break;
+    case 3: if constexpr (MAXMF >= 3) tile_body<FMT, STAGE, MAXMF, PF_MAX, 3>(A, J, sm, C); break;
+    case 4: if constexpr (MAXMF >= 4) tile_body<FMT, STAGE, MAXMF, PF_MAX, 4>(A, J, sm, C); break;
+    case 5: if constexpr (MAXMF >= 5) tile_body<FMT, STAGE, MAXMF, PF_MAX, 5>(A, J, sm, C); break;
+    default: if constexpr (MAXMF >= 6) tile_body<FMT, STAGE, MAXMF, PF_MAX, MAXMF>(A, J, sm, C); break;
   }
 }
 
@@ -245,7 +307,7 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
 // column blocks of one row tile share an XCD (and its L2 copy of the gathered
 // activation rows), and empty slots spread evenly over the XCDs.
 __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_routed,
-                                           int ncols_shared, TileJob& J) {
+                                           int ncols_shared, int rows_per_tile, TileJob& J) {
   const int b = blockIdx.x;
   const int slot = (b / (8 * NB)) * 8 + (b & 7);
   J.nb = (b >> 3) % NB;
@@ -255,42 +317,55 @@ __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_r
     J.shared = false;
     J.expert = t.x;
     J.start = A.offsets[t.x] + t.y;
-    J.cnt = min(BM, A.offsets[t.x + 1] - J.start);
+    J.cnt = min(rows_per_tile, A.offsets[t.x + 1] - J.start);
     return J.nb < ncols_routed;
   }
   const int s = slot - A.routed_slots;
   if (s >= A.shared_slots) return false;
   J.shared = true;
   J.expert = -1;
-  J.start = s * BM;
-  J.cnt = min(BM, A.T - J.start);
+  J.start = s * rows_per_tile;
+  J.cnt = min(rows_per_tile, A.T - J.start);
   return J.nb < ncols_shared;
 }
 
-template <int RF, int SF, int STAGE>
+template <int RF, int SF, int STAGE, int MAXMF, int PF>
 __global__ __launch_bounds__(256, 2) void ffn_kernel(FfnArgs A) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem<MAXMF> sm;
   const int NB = STAGE == 1 ? max(A.F, A.n_shared ? A.Fs : 0) / H_COLS_BLOCK : A.d / OUT_COLS_BLOCK;
   TileJob J;
   if (!decode_job(A, NB, STAGE == 1 ? A.F / H_COLS_BLOCK : NB,
-                  STAGE == 1 ? A.Fs / H_COLS_BLOCK : NB, J))
+                  STAGE == 1 ? A.Fs / H_COLS_BLOCK : NB, MAXMF * 16, J))
     return;
   if (J.shared)
-    run_tile<SF, STAGE>(A, J, sm);
+    run_tile<SF, STAGE, MAXMF, PF>(A, J, sm);
   else
-    run_tile<RF, STAGE>(A, J, sm);
+    run_tile<RF, STAGE, MAXMF, PF>(A, J, sm);
+}
+
+// Row tiles come from the route plan (at most BM = 96 rows each).  A call
+// with at most 16 or 32 tokens has at most that many rows per expert (a token
+// picks an expert once), so it runs a kernel built for 1 or 2 row fragments
+// with a deeper weight prefetch; shared-expert tiles then hold 16 or 32 tokens.
+template <int RF, int SF, int MAXMF, int PF>
+static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
+  FfnArgs a = a0;
+  a.shared_slots = a.n_shared ? (a.T + MAXMF * 16 - 1) / (MAXMF * 16) : 0;
+  const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
+  const int nb1 = max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_BLOCK;
+  const int nb2 = a.d / OUT_COLS_BLOCK;
+  ffn_kernel<RF, SF, 1, MAXMF, PF><<<slots * nb1, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ffn_kernel<RF, SF, 2, MAXMF, PF><<<slots * nb2, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int RF, int SF>
 static hipError_t launch_pair(const FfnArgs& a, hipStream_t s) {
-  const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
-  const int nb1 = max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_BLOCK;
-  const int nb2 = a.d / OUT_COLS_BLOCK;
-  ffn_kernel<RF, SF, 1><<<slots * nb1, 256, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  ffn_kernel<RF, SF, 2><<<slots * nb2, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (a.T <= 16) return launch_stages<RF, SF, 1, 4>(a, s);
+  if (a.T <= 32) return launch_stages<RF, SF, 2, 4>(a, s);
+  return launch_stages<RF, SF, BM / 16, 4>(a, s);
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
@@ -307,7 +382,7 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
 // Block = one row tile x 64 columns, one thread per column, rows in sequence.
 __global__ __launch_bounds__(64) void ffn_f32_stage1(FfnArgs A, int NB) {
   TileJob J;
-  if (!decode_job(A, NB, A.F / 64, A.n_shared ? A.Fs / 64 : 0, J)) return;
+  if (!decode_job(A, NB, A.F / 64, A.n_shared ? A.Fs / 64 : 0, BM, J)) return;
   const int Fw = J.shared ? A.Fs : A.F;
   const int j = J.nb * 64 + threadIdx.x;
   const float* blob = (const float*)(J.shared ? A.shared_blob
@@ -339,7 +414,7 @@ __global__ __launch_bounds__(64) void ffn_f32_stage1(FfnArgs A, int NB) {
 
 __global__ __launch_bounds__(64) void ffn_f32_stage2(FfnArgs A, int NB) {
   TileJob J;
-  if (!decode_job(A, NB, NB, NB, J)) return;
+  if (!decode_job(A, NB, NB, NB, BM, J)) return;
   const int Fw = J.shared ? A.Fs : A.F;
   const int n = J.nb * 64 + threadIdx.x;
   const float* blob = (const float*)(J.shared ? A.shared_blob
@@ -355,7 +430,9 @@ __global__ __launch_bounds__(64) void ffn_f32_stage2(FfnArgs A, int NB) {
   }
 }
 
-hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_f32(const FfnArgs& a0, hipStream_t s) {
+  FfnArgs a = a0;
+  a.shared_slots = a.n_shared ? (a.T + BM - 1) / BM : 0;
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
   const int nb1 = max(a.F, a.n_shared ? a.Fs : 0) / 64, nb2 = a.d / 64;
   ffn_f32_stage1<<<slots * nb1, 64, 0, s>>>(a, nb1);

@@ -19,7 +19,7 @@ namespace moe {
 //   stage 2 (down):    each wave owns 64 output columns, a block 256.
 // K advances in chunks of KC; one chunk of one wave's 64 weight rows is a
 // "wave tile", stored contiguously in the blob.
-constexpr int BM = 128;          // rows of an expert group per block (4 x 32)
+constexpr int BM = 96;           // rows of an expert group per row tile (6 x 16)
 constexpr int KC = 64;           // K per chunk (4 MFMA K-steps of 16)
 constexpr int WAVES = 4;         // waves per GEMM block
 constexpr int H_COLS_BLOCK = 128;  // stage-1 h columns per block
