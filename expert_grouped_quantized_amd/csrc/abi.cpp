@@ -117,7 +117,7 @@ inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
 //   I4  : dword (code + 8 per nibble, element i in nibble i) at
 //         ((f/2)*64 + lane)*16 + ((f%2)*2 + s)*4; then per row c the 8 fp16
 //         group scales [f][s] at 2048 + c*16
-//   I8  : 8 bytes (code + 128) at (f*64 + lane)*16 + s*8
+//   I8  : 8 int8 codes at (f*64 + lane)*16 + s*8
 struct OutIO {  // canonical outputs of unpacking
   uint8_t* q;
   uint8_t* s;
@@ -142,9 +142,8 @@ bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) 
             word |= (uint32_t)(c + 8) << (4 * i);
           }
           memcpy(dst + ((size_t)(f >> 1) * 64 + lane) * 16 + ((f & 1) * 2 + s) * 4, &word, 4);
-        } else {  // I8
-          uint8_t* o = dst + ((size_t)f * 64 + lane) * 16 + s * 8;
-          for (int i = 0; i < 8; i++) o[i] = (uint8_t)((int)((const int8_t*)M.q)[r * M.K + k0 + i] + 128);
+        } else {  // I8: the codes as they are
+          memcpy(dst + ((size_t)f * 64 + lane) * 16 + s * 8, (const int8_t*)M.q + r * M.K + k0, 8);
         }
       }
     }
@@ -182,8 +181,7 @@ void unpack_tile(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int6
             b = (k & 1) ? (uint8_t)((b & 0x0f) | (nib << 4)) : (uint8_t)((b & 0xf0) | nib);
           }
         } else {
-          const uint8_t* o = src + ((size_t)f * 64 + lane) * 16 + s * 8;
-          for (int i = 0; i < 8; i++) ((int8_t*)out[f].q)[r * K + k0 + i] = (int8_t)((int)o[i] - 128);
+          memcpy((int8_t*)out[f].q + r * K + k0, src + ((size_t)f * 64 + lane) * 16 + s * 8, 8);
         }
       }
     }

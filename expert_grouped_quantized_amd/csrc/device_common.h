@@ -42,6 +42,45 @@ __device__ __forceinline__ int lds_a_index(int row, int chunk) {
   return row * 64 + ((chunk ^ (row & 7)) << 3);  // in bf16 elements
 }
 
+// Byte n of a dword as a float, one v_cvt_f32_ubyte<n> each (the compiler
+// otherwise splits the byte extraction into a separate bit-field extract).
+__device__ __forceinline__ float ubyte0_f(uint32_t x) {
+  float r;
+  asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ float ubyte1_f(uint32_t x) {
+  float r;
+  asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ float ubyte2_f(uint32_t x) {
+  float r;
+  asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ float ubyte3_f(uint32_t x) {
+  float r;
+  asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Signed byte n of a dword as a float: the SDWA form selects and sign-extends
+// the byte inside the convert.
+#define MOE_SBYTE_F(N)                                                                     \
+  __device__ __forceinline__ float sbyte##N##_f(uint32_t x) {                              \
+    float r;                                                                               \
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_" #N \
+        : "=v"(r)                                                                          \
+        : "v"(x));                                                                         \
+    return r;                                                                              \
+  }
+MOE_SBYTE_F(0)
+MOE_SBYTE_F(1)
+MOE_SBYTE_F(2)
+MOE_SBYTE_F(3)
+#undef MOE_SBYTE_F
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 }  // namespace moe

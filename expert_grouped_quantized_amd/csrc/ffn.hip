@@ -63,19 +63,17 @@ struct WTile<MOE_I4_G32> {
     const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
     const uint32_t lo = q & 0x0f0f0f0fu, hi = (q >> 4) & 0x0f0f0f0fu;
     u32x4_t r;
-    r[0] = pack_bf16x2(fmaf((float)(lo & 0xff), scale, bias), fmaf((float)(hi & 0xff), scale, bias));
-    r[1] = pack_bf16x2(fmaf((float)((lo >> 8) & 0xff), scale, bias),
-                       fmaf((float)((hi >> 8) & 0xff), scale, bias));
-    r[2] = pack_bf16x2(fmaf((float)((lo >> 16) & 0xff), scale, bias),
-                       fmaf((float)((hi >> 16) & 0xff), scale, bias));
-    r[3] = pack_bf16x2(fmaf((float)(lo >> 24), scale, bias), fmaf((float)(hi >> 24), scale, bias));
+    r[0] = pack_bf16x2(fmaf(ubyte0_f(lo), scale, bias), fmaf(ubyte0_f(hi), scale, bias));
+    r[1] = pack_bf16x2(fmaf(ubyte1_f(lo), scale, bias), fmaf(ubyte1_f(hi), scale, bias));
+    r[2] = pack_bf16x2(fmaf(ubyte2_f(lo), scale, bias), fmaf(ubyte2_f(hi), scale, bias));
+    r[3] = pack_bf16x2(fmaf(ubyte3_f(lo), scale, bias), fmaf(ubyte3_f(hi), scale, bias));
     return r;
   }
 };
 
 template <>
 struct WTile<MOE_I8_ROW> {
-  u32x4_t v[4];  // [frag]; dwords 2s, 2s+1 hold 8 bytes = code + 128
+  u32x4_t v[4];  // [frag]; dwords 2s, 2s+1 hold 8 int8 codes
   __device__ __forceinline__ void load(const uint8_t* t, int lane) {
 #pragma unroll
     for (int j = 0; j < 4; j++) v[j] = ((const u32x4_t*)t)[j * 64 + lane];
@@ -83,10 +81,10 @@ struct WTile<MOE_I8_ROW> {
   __device__ __forceinline__ u32x4_t frag(int f, int s) const {
     const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
     u32x4_t r;
-    r[0] = pack_bf16x2((float)(w0 & 0xff) - 128.0f, (float)((w0 >> 8) & 0xff) - 128.0f);
-    r[1] = pack_bf16x2((float)((w0 >> 16) & 0xff) - 128.0f, (float)(w0 >> 24) - 128.0f);
-    r[2] = pack_bf16x2((float)(w1 & 0xff) - 128.0f, (float)((w1 >> 8) & 0xff) - 128.0f);
-    r[3] = pack_bf16x2((float)((w1 >> 16) & 0xff) - 128.0f, (float)(w1 >> 24) - 128.0f);
+    r[0] = pack_bf16x2(sbyte0_f(w0), sbyte1_f(w0));
+    r[1] = pack_bf16x2(sbyte2_f(w0), sbyte3_f(w0));
+    r[2] = pack_bf16x2(sbyte0_f(w1), sbyte1_f(w1));
+    r[3] = pack_bf16x2(sbyte2_f(w1), sbyte3_f(w1));
     return r;
   }
 };
