@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
     p.add_argument("--workload", choices=("both", "prefill", "decode"), default="both",
                    help="limit the run to one workload (for per-workload profiles)")
     return p.parse_args()
@@ -212,6 +214,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     prefill = decode = roof_p = roof_d = pre_inputs = None
     if args.workload in ("both", "prefill"):
         prefill, roof_p, pre_inputs = run_prefill(args, torch, W)

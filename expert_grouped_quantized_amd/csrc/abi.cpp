@@ -105,6 +105,8 @@ inline int i4_code(const MatIO& m, int64_t r, int64_t k) {
   int n = (k & 1) ? (b >> 4) : (b & 15);
   return n >= 8 ? n - 16 : n;
 }
+// nibble of a packed lane dword that holds element i (0..7) of the lane's 8
+inline int i4_nibble(int i) { return (i & 1) ? 4 + (i >> 1) : (i >> 1); }
 inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
   return ((const uint16_t*)m.s)[r * (m.K / 32) + k / 32];
 }
@@ -114,7 +116,7 @@ inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
 // K step s (0..1) covers 32 K.  Lane l of the consuming wave holds row
 // c = l % 16 and K offsets 32*s + 8*(l/16) .. +7.
 //   BF16: 16-byte piece (f*2 + s, lane) at ((f*2 + s)*64 + lane)*16
-//   I4  : dword (code + 8 per nibble, element i in nibble i) at
+//   I4  : dword (code + 8 per nibble; element 2j in nibble j, 2j+1 in j+4) at
 //         ((f/2)*64 + lane)*16 + ((f%2)*2 + s)*4; then per row c the 8 fp16
 //         group scales [f][s] at 2048 + c*16
 //   I8  : 8 int8 codes at (f*64 + lane)*16 + s*8
@@ -135,11 +137,11 @@ bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) 
         if (fmt == MOE_BF16) {
           memcpy(dst + ((size_t)(f * 2 + s) * 64 + lane) * 16, (const uint16_t*)M.q + r * M.K + k0, 16);
         } else if (fmt == MOE_I4_G32) {
-          uint32_t word = 0;
+          uint32_t word = 0;  // element 2j in nibble j, element 2j+1 in nibble j+4
           for (int i = 0; i < 8; i++) {
             const int c = i4_code(M, r, k0 + i);
             if (c < -7) return false;
-            word |= (uint32_t)(c + 8) << (4 * i);
+            word |= (uint32_t)(c + 8) << (4 * i4_nibble(i));
           }
           memcpy(dst + ((size_t)(f >> 1) * 64 + lane) * 16 + ((f & 1) * 2 + s) * 4, &word, 4);
         } else {  // I8: the codes as they are
@@ -174,7 +176,7 @@ void unpack_tile(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int6
           uint32_t word;
           memcpy(&word, src + ((size_t)(f >> 1) * 64 + lane) * 16 + ((f & 1) * 2 + s) * 4, 4);
           for (int i = 0; i < 8; i++) {
-            const int c = (int)((word >> (4 * i)) & 15) - 8;
+            const int c = (int)((word >> (4 * i4_nibble(i))) & 15) - 8;
             const int64_t k = k0 + i;
             uint8_t& b = out[f].q[r * (K / 2) + k / 2];
             const uint8_t nib = (uint8_t)(c & 15);
@@ -230,41 +232,37 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
   const size_t tb = tile_bytes(fmt);
   const int64_t nk1 = d / KC, nk2 = F / KC;
   const MatIO G{fmt, F, d, io.g, io.gs}, U{fmt, F, d, io.u, io.us}, Dn{fmt, d, F, io.dn, io.ds};
-  // W1 wave tile (nb, w), h columns c0 = nb*128 + w*32: fragments 0, 1 = gate
-  // rows c0 + 16*(f%2) + c, fragments 2, 3 = up rows of the same columns
+  // W1 run j (h columns c0 = 32*j): fragments 0, 1 = gate rows c0 + 16*(f%2) + c,
+  // fragments 2, 3 = up rows of the same columns; runs in order, then K chunks
   const MatIO* const m1[4] = {&G, &G, &U, &U};
   const OutIO og{(uint8_t*)io.g, (uint8_t*)io.gs}, ou{(uint8_t*)io.u, (uint8_t*)io.us};
   const OutIO o1[4] = {og, og, ou, ou};
-  for (int64_t nb = 0; nb < F / H_COLS_BLOCK; nb++) {
-    for (int w = 0; w < WAVES; w++) {
-      const int64_t c0 = nb * H_COLS_BLOCK + w * 32;
-      auto row_of = [c0](int f, int c) { return c0 + (f & 1) * 16 + c; };
-      for (int64_t kc = 0; kc < nk1; kc++) {
-        uint8_t* t = blob + ((size_t)(nb * WAVES + w) * nk1 + kc) * tb;
-        if (!unpack) {
-          if (!pack_tile(m1, row_of, kc, t)) return false;
-        } else {
-          unpack_tile(m1, o1, row_of, kc, t);
-        }
+  for (int64_t j = 0; j < F / H_COLS_WAVE; j++) {
+    const int64_t c0 = j * H_COLS_WAVE;
+    auto row_of = [c0](int f, int c) { return c0 + (f & 1) * 16 + c; };
+    for (int64_t kc = 0; kc < nk1; kc++) {
+      uint8_t* t = blob + ((size_t)j * nk1 + kc) * tb;
+      if (!unpack) {
+        if (!pack_tile(m1, row_of, kc, t)) return false;
+      } else {
+        unpack_tile(m1, o1, row_of, kc, t);
       }
     }
   }
-  // W2 wave tile (nb, w): fragment f = down rows nb*256 + w*64 + 16*f + c
+  // W2 run j: fragment f = down rows 64*j + 16*f + c
   uint8_t* w2 = blob + w1b;
   const MatIO* const m2[4] = {&Dn, &Dn, &Dn, &Dn};
   const OutIO od{(uint8_t*)io.dn, (uint8_t*)io.ds};
   const OutIO o2[4] = {od, od, od, od};
-  for (int64_t nb = 0; nb < d / OUT_COLS_BLOCK; nb++) {
-    for (int w = 0; w < WAVES; w++) {
-      const int64_t rbase = nb * OUT_COLS_BLOCK + w * 64;
-      auto row_of = [rbase](int f, int c) { return rbase + f * 16 + c; };
-      for (int64_t kc = 0; kc < nk2; kc++) {
-        uint8_t* t = w2 + ((size_t)(nb * WAVES + w) * nk2 + kc) * tb;
-        if (!unpack) {
-          if (!pack_tile(m2, row_of, kc, t)) return false;
-        } else {
-          unpack_tile(m2, o2, row_of, kc, t);
-        }
+  for (int64_t j = 0; j < d / OUT_COLS_WAVE; j++) {
+    const int64_t rbase = j * OUT_COLS_WAVE;
+    auto row_of = [rbase](int f, int c) { return rbase + f * 16 + c; };
+    for (int64_t kc = 0; kc < nk2; kc++) {
+      uint8_t* t = w2 + ((size_t)j * nk2 + kc) * tb;
+      if (!unpack) {
+        if (!pack_tile(m2, row_of, kc, t)) return false;
+      } else {
+        unpack_tile(m2, o2, row_of, kc, t);
       }
     }
   }
@@ -462,6 +460,7 @@ moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* 
   a.routed_blob = (const uint8_t*)routed_blob;
   a.shared_blob = (const uint8_t*)shared_blob;
   a.h_routed = w + L.h_routed; a.h_shared = w + L.h_shared;
+  a.x16 = (uint16_t*)(w + L.x16); a.xscale = (float*)(w + L.xexp);
   a.out_assign = out_assign; a.shared_out = shared_out;
   hipStream_t s = (hipStream_t)stream;
   return device_result(D->act == MOE_F32 ? launch_ffn_f32(a, s) : launch_ffn_bf16(a, s),

@@ -11,6 +11,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // Two floats -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -80,6 +82,33 @@ MOE_SBYTE_F(1)
 MOE_SBYTE_F(2)
 MOE_SBYTE_F(3)
 #undef MOE_SBYTE_F
+
+// (x & m) | o in one instruction (the masks live in registers: gfx9 VOP3
+// encodings take no literal operands).
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
+  return r;
+}
+
+// Signed bytes (0,1) or (2,3) of a dword as two fp16 values (exact): each
+// SDWA convert sign-extends one byte and writes one half of the result.
+__device__ __forceinline__ uint32_t sbytes01_f16x2(uint32_t x) {
+  uint32_t r;
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+      : "=v"(r) : "v"(x));
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
+      : "+v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ uint32_t sbytes23_f16x2(uint32_t x) {
+  uint32_t r;
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+      : "=v"(r) : "v"(x));
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+      : "+v"(r) : "v"(x));
+  return r;
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 

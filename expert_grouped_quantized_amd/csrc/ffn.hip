@@ -30,43 +30,86 @@ __device__ __forceinline__ f32x4_t mfma16x16(const u32x4_t& a, const u32x4_t& b,
                                                  __builtin_bit_cast(bf16x8_f, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4_t mfma16x16_f16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Weight loads; NT streams them past the caches (non-temporal) for weights that
+// one row tile reads once, so they do not evict activation rows.
+template <bool NT>
+__device__ __forceinline__ u32x4_t ldw(const uint8_t* base, int i) {
+  if (NT) return __builtin_nontemporal_load((const u32x4_t*)base + i);
+  return ((const u32x4_t*)base)[i];
+}
+
 // ---- weight registers of one wave tile (64 rows x 64 K) -------------------
 // Fragment f (0..3) is 16 weight rows; step s (0..1) is 32 K.  Lane l holds
 // row l % 16 of each fragment and K elements 32*s + 8*(l/16) .. +7.
+// frag() returns the 8 weights as bf16 (for bf16 MFMA), frag16() as fp16.
 template <int FMT>
 struct WTile;
 
 template <>
 struct WTile<MOE_BF16> {
   u32x4_t v[8];  // [frag][step]
+  template <bool NT>
   __device__ __forceinline__ void load(const uint8_t* t, int lane) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = ((const u32x4_t*)t)[j * 64 + lane];
+    for (int j = 0; j < 8; j++) v[j] = ldw<NT>(t, j * 64 + lane);
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s) const { return v[f * 2 + s]; }
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t, uint32_t) const {
+    return v[f * 2 + s];  // never used: bf16 weights run bf16 MFMA
+  }
 };
 
 template <>
 struct WTile<MOE_I4_G32> {
-  u32x4_t v[2];  // [frag pair]; dword (f%2)*2 + s holds 8 nibbles = code + 8
-  u32x4_t sc;    // 8 fp16 group scales, index f*2 + s (group = step)
+  // [frag pair]; dword (f%2)*2 + s holds the lane's 8 codes + 8: element 2j in
+  // nibble j, element 2j+1 in nibble j+4 (so nibbles j and j+4, at bits 4j and
+  // 16+4j, are the pair that one packed fp16 register takes)
+  u32x4_t v[2];
+  u32x4_t sc;  // 8 fp16 group scales, index f*2 + s (group = step)
+  template <bool NT>
   __device__ __forceinline__ void load(const uint8_t* t, int lane) {
-    v[0] = ((const u32x4_t*)t)[lane];
-    v[1] = ((const u32x4_t*)t)[64 + lane];
-    sc = ((const u32x4_t*)(t + 2048))[lane & 15];
+    v[0] = ldw<NT>(t, lane);
+    v[1] = ldw<NT>(t, 64 + lane);
+    sc = ldw<NT>(t + 2048, lane & 15);
   }
-  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+  __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
     const int si = f * 2 + s;
     const uint32_t sw = sc[si >> 1];
-    const float scale = f16_bits_to_f32((uint16_t)((si & 1) ? (sw >> 16) : (sw & 0xffffu)));
+    return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
+  }
+  // bf16(code * scale): code + 8 as a float, one FMA with the scale (exact in
+  // fp32), rounded to nearest even by the pack
+  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+    const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
     const float bias = -8.0f * scale;
     const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
     const uint32_t lo = q & 0x0f0f0f0fu, hi = (q >> 4) & 0x0f0f0f0fu;
     u32x4_t r;
-    r[0] = pack_bf16x2(fmaf(ubyte0_f(lo), scale, bias), fmaf(ubyte0_f(hi), scale, bias));
-    r[1] = pack_bf16x2(fmaf(ubyte1_f(lo), scale, bias), fmaf(ubyte1_f(hi), scale, bias));
-    r[2] = pack_bf16x2(fmaf(ubyte2_f(lo), scale, bias), fmaf(ubyte2_f(hi), scale, bias));
-    r[3] = pack_bf16x2(fmaf(ubyte3_f(lo), scale, bias), fmaf(ubyte3_f(hi), scale, bias));
+    r[0] = pack_bf16x2(fmaf(ubyte0_f(lo), scale, bias), fmaf(ubyte2_f(lo), scale, bias));
+    r[1] = pack_bf16x2(fmaf(ubyte0_f(hi), scale, bias), fmaf(ubyte2_f(hi), scale, bias));
+    r[2] = pack_bf16x2(fmaf(ubyte1_f(lo), scale, bias), fmaf(ubyte3_f(lo), scale, bias));
+    r[3] = pack_bf16x2(fmaf(ubyte1_f(hi), scale, bias), fmaf(ubyte3_f(hi), scale, bias));
+    return r;
+  }
+  // fp16(code * scale): a nibble pair OR-ed into two fp16 mantissas is
+  // (1024 + code + 8) each; one packed subtract makes the codes exact, one
+  // packed multiply by the fp16 scale rounds each product to nearest even
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t m, uint32_t o) const {
+    const uint32_t sb = scale_bits(f, s);
+    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
+    const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), m, o));
+      r[j] = __builtin_bit_cast(uint32_t, (t + off) * s2);
+    }
     return r;
   }
 };
@@ -74,9 +117,10 @@ struct WTile<MOE_I4_G32> {
 template <>
 struct WTile<MOE_I8_ROW> {
   u32x4_t v[4];  // [frag]; dwords 2s, 2s+1 hold 8 int8 codes
+  template <bool NT>
   __device__ __forceinline__ void load(const uint8_t* t, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) v[j] = ((const u32x4_t*)t)[j * 64 + lane];
+    for (int j = 0; j < 4; j++) v[j] = ldw<NT>(t, j * 64 + lane);
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s) const {
     const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
@@ -86,6 +130,10 @@ struct WTile<MOE_I8_ROW> {
     r[2] = pack_bf16x2(sbyte0_f(w1), sbyte1_f(w1));
     r[3] = pack_bf16x2(sbyte2_f(w1), sbyte3_f(w1));
     return r;
+  }
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t, uint32_t) const {
+    const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
+    return u32x4_t{sbytes01_f16x2(w0), sbytes23_f16x2(w0), sbytes01_f16x2(w1), sbytes23_f16x2(w1)};
   }
 };
 
@@ -99,6 +147,7 @@ template <int MAXMF>
 struct Smem {
   uint16_t a[2][MAXMF * 16 * 64];
   float wrow[MAXMF * 16];
+  float xs[MAXMF * 16];  // power of two to undo on fp16-staged rows
   int src[MAXMF * 16];
 };
 
@@ -109,21 +158,21 @@ __device__ __forceinline__ float silu_fast(float g) {
 // Per-tile constants shared by the setup and the main loop.
 struct TileCtx {
   int Fw, nk;
+  int run;              // this wave's run of 64 weight rows
   const uint8_t* sect;  // W1 or W2 section of this expert's blob
   const uint8_t* wt;    // this wave's run of weight tiles
   const uint16_t* arow[3];
-  bool a_loader;
 };
 
-template <int FMT, int STAGE, int MAXMF, int PF_MAX, int NMF>
+template <int FMT, int STAGE, int MAXMF, int PF_MAX, int NMF, bool F16, bool NT>
 __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm,
                                           const TileCtx& C) {
   // a bf16 wave tile is 4x the bytes (and registers) of an int4 one
   constexpr int PF = FMT == MOE_BF16 ? 2 : PF_MAX;
   constexpr int ROWS = MAXMF * 16;
-  constexpr int PIECES = ROWS * 8;
-  constexpr int PPT = PIECES >= 256 ? PIECES / 256 : 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
+  constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
+  const int tid = threadIdx.x, lane = tid & 63;
   const int nk = C.nk;
   const size_t tb = tile_bytes(FMT);
   const int c8 = tid & 7;
@@ -144,11 +193,12 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       dst[j] = C.arow[j] ? *(const u32x4_t*)(C.arow[j] + kc * KC) : u32x4_t{0, 0, 0, 0};
   };
   auto store_a = [&](uint16_t* dst, const u32x4_t (&src)[PPT]) {
-    if (C.a_loader) {
 #pragma unroll
-      for (int j = 0; j < PPT; j++) *(u32x4_t*)(dst + lds_a_index((tid >> 3) + 32 * j, c8)) = src[j];
-    }
+    for (int j = 0; j < PPT; j++)
+      if (tid + WAVES * 64 * j < PIECES)
+        *(u32x4_t*)(dst + lds_a_index((tid >> 3) + 8 * WAVES * j, c8)) = src[j];
   };
+  const uint32_t nib_mask = 0x000f000fu, f16_magic = 0x64006400u;
   auto compute = [&](const uint16_t* as, const WTile<FMT>& w) {
 #pragma unroll
     for (int s = 0; s < 2; s++) {
@@ -159,9 +209,15 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
         av[i] = *(const u32x4_t*)(as + lds_a_index(i * 16 + (lane & 15), ch));
 #pragma unroll
       for (int f = 0; f < 4; f++) {
-        const u32x4_t b = w.frag(f, s);
+        if (F16) {
+          const u32x4_t b = w.frag16(f, s, nib_mask, f16_magic);
 #pragma unroll
-        for (int i = 0; i < NMF; i++) acc[i][f] = mfma16x16(av[i], b, acc[i][f]);
+          for (int i = 0; i < NMF; i++) acc[i][f] = mfma16x16_f16(av[i], b, acc[i][f]);
+        } else {
+          const u32x4_t b = w.frag(f, s);
+#pragma unroll
+          for (int i = 0; i < NMF; i++) acc[i][f] = mfma16x16(av[i], b, acc[i][f]);
+        }
       }
     }
   };
@@ -170,7 +226,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
   WTile<FMT> ring[PF];
 #pragma unroll
   for (int p = 0; p < PF; p++)
-    if (p < nk) ring[p].load(C.wt + (size_t)p * tb, lane);
+    if (p < nk) ring[p].template load<NT>(C.wt + (size_t)p * tb, lane);
   load_a(0, areg[0]);
   if (1 < nk) load_a(1, areg[1]);
   store_a(sm.a[0], areg[0]);
@@ -182,7 +238,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       if (kc < nk) {  // block-uniform
         if (kc + 2 < nk) load_a(kc + 2, areg[p & 1]);
         compute(sm.a[p & 1], ring[p]);
-        if (kc + PF < nk) ring[p].load(C.wt + (size_t)(kc + PF) * tb, lane);
+        if (kc + PF < nk) ring[p].template load<NT>(C.wt + (size_t)(kc + PF) * tb, lane);
         if (kc + 1 < nk) store_a(sm.a[(p + 1) & 1], areg[(p + 1) & 1]);
         __syncthreads();
       }
@@ -200,7 +256,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
     uint16_t* hout = (uint16_t*)(J.shared ? A.h_shared : A.h_routed);
 #pragma unroll
     for (int f = 0; f < 2; f++) {  // fragments 0,1 = gate, 2,3 = up of the same columns
-      const int col = J.nb * H_COLS_BLOCK + wave * 32 + f * 16 + (lane & 15);
+      const int col = C.run * H_COLS_WAVE + f * 16 + (lane & 15);
       float sg = 1.0f, su = 1.0f;
       if (FMT == MOE_I8_ROW) {
         sg = f16_bits_to_f32(rscale[col]);
@@ -212,7 +268,11 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
         for (int r = 0; r < 4; r++) {
           const int m = i * 16 + 4 * (lane >> 4) + r;
           if (m < J.cnt) {
-            const float g = acc[i][f][r] * sg, u = acc[i][f + 2][r] * su;
+            float g = acc[i][f][r] * sg, u = acc[i][f + 2][r] * su;
+            if (F16) {
+              g *= sm.xs[m];
+              u *= sm.xs[m];
+            }
             const float h = sm.wrow[m] * silu_fast(g) * u;
             hout[(size_t)(J.start + m) * Fw + col] = (uint16_t)(pack_bf16x2(h, 0.0f) & 0xffffu);
           }
@@ -223,7 +283,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
     float* out = J.shared ? A.shared_out : A.out_assign;
 #pragma unroll
     for (int f = 0; f < 4; f++) {
-      const int col = J.nb * OUT_COLS_BLOCK + wave * 64 + f * 16 + (lane & 15);
+      const int col = C.run * OUT_COLS_WAVE + f * 16 + (lane & 15);
       const float sc = FMT == MOE_I8_ROW ? f16_bits_to_f32(rscale[col]) : 1.0f;
 #pragma unroll
       for (int i = 0; i < NMF; i++) {
@@ -237,27 +297,34 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
   }
 }
 
-template <int FMT, int STAGE, int MAXMF, int PF_MAX>
+// F16: stage-1 tile on fp16 MFMA, A rows from the fp16 copy of the
+// activations (scaled per token by a power of two, undone in the epilogue).
+template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
 __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm) {
   constexpr int ROWS = MAXMF * 16;
   constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
-  constexpr int PPT = PIECES >= 256 ? PIECES / 256 : 1;
+  constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
   static_assert(PPT <= 3, "A staging holds at most 3 pieces per thread");
   const int tid = threadIdx.x, wave = tid >> 6;
   TileCtx C;
   C.Fw = J.shared ? A.Fs : A.F;
   const int K = STAGE == 1 ? A.d : C.Fw;
   C.nk = K / KC;
+  C.run = J.nb * WAVES + wave;
+  // the ABI requires ffn widths % 128 and d % 256: every wave of a block has
+  // a run of weight rows
+  static_assert(WAVES * H_COLS_WAVE == H_COLS_BLOCK && WAVES * OUT_COLS_WAVE == OUT_COLS_BLOCK,
+                "a block covers whole 64-row weight runs of every matrix");
   const size_t tb = tile_bytes(FMT);
   const uint8_t* blob = J.shared ? A.shared_blob
                                  : A.routed_blob + (size_t)J.expert * expert_bytes(FMT, A.d, A.F);
   C.sect = STAGE == 1 ? blob : blob + w1_bytes(FMT, A.d, C.Fw);
-  C.wt = C.sect + (size_t)(J.nb * WAVES + wave) * C.nk * tb;
+  C.wt = C.sect + (size_t)C.run * C.nk * tb;
 
   // rows of this tile: source row of the activations and folded router weight
-  for (int m = tid; m < ROWS; m += 256) {
+  for (int m = tid; m < ROWS; m += WAVES * 64) {
     int src = -1;
-    float wf = 0.0f;
+    float wf = 0.0f, xs = 1.0f;
     if (m < J.cnt) {
       if (STAGE == 1) {
         if (J.shared) {
@@ -268,35 +335,36 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
           src = f / A.k;
           wf = A.topk_w[f];
         }
+        if (F16) xs = A.xscale[src];
       } else {
         src = J.start + m;
       }
     }
     sm.src[m] = src;
     sm.wrow[m] = wf;
+    sm.xs[m] = xs;
   }
   __syncthreads();
 
-  const uint16_t* abase = STAGE == 1 ? (const uint16_t*)A.hidden
+  const uint16_t* abase = STAGE == 1 ? (F16 ? (const uint16_t*)A.x16 : (const uint16_t*)A.hidden)
                                      : (const uint16_t*)(J.shared ? A.h_shared : A.h_routed);
   const size_t astride = STAGE == 1 ? (size_t)A.d : (size_t)C.Fw;
-  C.a_loader = tid < PIECES;
 #pragma unroll
   for (int j = 0; j < 3; j++) {
-    const int r = (tid >> 3) + 32 * j;
-    const int s = (j < PPT && C.a_loader && r < ROWS) ? sm.src[r] : -1;
+    const int r = (tid >> 3) + 8 * WAVES * j;  // piece tid + 64*WAVES*j: row r, 16-byte chunk tid % 8
+    const int s = (j < PPT && tid + WAVES * 64 * j < PIECES) ? sm.src[r] : -1;
     C.arow[j] = s >= 0 ? abase + (size_t)s * astride + (tid & 7) * 8 : nullptr;
   }
   // the number of live 16-row fragments is a compile-time constant of the
   // loop, so every step issues its A reads together and runs branch-free
   const int nmf = (J.cnt + 15) >> 4;
   switch (nmf) {
-    case 1: tile_body<FMT, STAGE, MAXMF, PF_MAX, 1>(A, J, sm, C); break;
-    case 2: if constexpr (MAXMF >= 2) tile_body<FMT, STAGE, MAXMF, PF_MAX, 2>(A, J, sm, C); break;
-    case 3: if constexpr (MAXMF >= 3) tile_body<FMT, STAGE, MAXMF, PF_MAX, 3>(A, J, sm, C); break;
-    case 4: if constexpr (MAXMF >= 4) tile_body<FMT, STAGE, MAXMF, PF_MAX, 4>(A, J, sm, C); break;
-    case 5: if constexpr (MAXMF >= 5) tile_body<FMT, STAGE, MAXMF, PF_MAX, 5>(A, J, sm, C); break;
-    default: if constexpr (MAXMF >= 6) tile_body<FMT, STAGE, MAXMF, PF_MAX, MAXMF>(A, J, sm, C); break;
+    case 1: tile_body<FMT, STAGE, MAXMF, PF_MAX, 1, F16, NT>(A, J, sm, C); break;
+    case 2: if constexpr (MAXMF >= 2) tile_body<FMT, STAGE, MAXMF, PF_MAX, 2, F16, NT>(A, J, sm, C); break;
+    case 3: if constexpr (MAXMF >= 3) tile_body<FMT, STAGE, MAXMF, PF_MAX, 3, F16, NT>(A, J, sm, C); break;
+    case 4: if constexpr (MAXMF >= 4) tile_body<FMT, STAGE, MAXMF, PF_MAX, 4, F16, NT>(A, J, sm, C); break;
+    case 5: if constexpr (MAXMF >= 5) tile_body<FMT, STAGE, MAXMF, PF_MAX, 5, F16, NT>(A, J, sm, C); break;
+    default: if constexpr (MAXMF >= 6) tile_body<FMT, STAGE, MAXMF, PF_MAX, MAXMF, F16, NT>(A, J, sm, C); break;
   }
 }
 
@@ -327,18 +395,71 @@ __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_r
   return J.nb < ncols_shared;
 }
 
+// column blocks of a matrix with `runs` 64-row weight runs
+__host__ __device__ __forceinline__ int col_blocks(int runs) { return (runs + WAVES - 1) / WAVES; }
+
 template <int RF, int SF, int STAGE, int MAXMF, int PF>
-__global__ __launch_bounds__(256, 2) void ffn_kernel(FfnArgs A) {
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   __shared__ __attribute__((aligned(16))) Smem<MAXMF> sm;
-  const int NB = STAGE == 1 ? max(A.F, A.n_shared ? A.Fs : 0) / H_COLS_BLOCK : A.d / OUT_COLS_BLOCK;
+  const int nr = STAGE == 1 ? col_blocks(A.F / H_COLS_WAVE) : col_blocks(A.d / OUT_COLS_WAVE);
+  const int ns = STAGE == 1 ? (A.n_shared ? col_blocks(A.Fs / H_COLS_WAVE) : 0) : nr;
   TileJob J;
-  if (!decode_job(A, NB, STAGE == 1 ? A.F / H_COLS_BLOCK : NB,
-                  STAGE == 1 ? A.Fs / H_COLS_BLOCK : NB, MAXMF * 16, J))
-    return;
+  if (!decode_job(A, max(nr, ns), nr, ns, MAXMF * 16, J)) return;
+  // int4 routed layers run gate/up on fp16 MFMA (the fp16 activation copy
+  // exists); int8 shared tiles of such a layer follow; bf16 weights stay bf16
+  constexpr bool X16 = RF == MOE_I4_G32;
+  // Routed weights of a small-T call are read exactly once: stream them.  The
+  // shared expert's weights are re-read by every row tile, and a prefill
+  // expert can span two tiles: keep those cacheable.
+  constexpr bool NT_ROUTED = MAXMF <= 2, NT_SHARED = false;
   if (J.shared)
-    run_tile<SF, STAGE, MAXMF, PF>(A, J, sm);
+    run_tile<SF, STAGE, MAXMF, PF, STAGE == 1 && X16 && SF == MOE_I8_ROW, NT_SHARED>(A, J, sm);
   else
-    run_tile<RF, STAGE, MAXMF, PF>(A, J, sm);
+    run_tile<RF, STAGE, MAXMF, PF, STAGE == 1 && X16, NT_ROUTED>(A, J, sm);
+}
+
+// Activations of an int4 layer as fp16: each token row is scaled by 2^-e so
+// its largest magnitude lies in [2^14, 2^15) -- every bf16 value of the row is
+// then exact in fp16 unless it is 2^-28 below the row's largest -- and 2^e is
+// kept for the gate/up epilogue.  One wave per row.
+__global__ __launch_bounds__(256) void x_to_f16_kernel(int T, int d, const uint16_t* __restrict__ x,
+                                                       uint16_t* __restrict__ x16,
+                                                       float* __restrict__ xscale) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const u32x4_t* src = (const u32x4_t*)(x + (size_t)t * d);
+  const int pieces = d / 8;
+  uint32_t mx = 0;  // largest |x| as float bits (non-negative floats order as integers)
+  for (int p = lane; p < pieces; p += 64) {
+    const u32x4_t v = src[p];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t a = (v[j] << 16) & 0x7fffffffu, b = v[j] & 0x7fff0000u;
+      mx = max(mx, max(a, b));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  int e = 0;
+  if (mx != 0) {
+    const int ex = (int)(mx >> 23) - 127;  // floor(log2 max|x|) for normal values
+    e = max(ex, -126) - 14;
+    e = max(e, -100);
+  }
+  const float down = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+  if (lane == 0) xscale[t] = __uint_as_float((uint32_t)(127 + e) << 23);
+  u32x4_t* dst = (u32x4_t*)(x16 + (size_t)t * d);
+  for (int p = lane; p < pieces; p += 64) {
+    const u32x4_t v = src[p];
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f16x2_t h = {(_Float16)(bf16_lo(v[j]) * down), (_Float16)(bf16_hi(v[j]) * down)};
+      o[j] = __builtin_bit_cast(uint32_t, h);
+    }
+    dst[p] = o;
+  }
 }
 
 // Row tiles come from the route plan (at most BM = 96 rows each).  A call
@@ -350,12 +471,18 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
   FfnArgs a = a0;
   a.shared_slots = a.n_shared ? (a.T + MAXMF * 16 - 1) / (MAXMF * 16) : 0;
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
-  const int nb1 = max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_BLOCK;
-  const int nb2 = a.d / OUT_COLS_BLOCK;
-  ffn_kernel<RF, SF, 1, MAXMF, PF><<<slots * nb1, 256, 0, s>>>(a);
+  const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
+  const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
+  if (RF == MOE_I4_G32) {
+    x_to_f16_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.T, a.d, (const uint16_t*)a.hidden, a.x16,
+                                                   a.xscale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ffn_kernel<RF, SF, 1, MAXMF, PF><<<slots * nb1, WAVES * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ffn_kernel<RF, SF, 2, MAXMF, PF><<<slots * nb2, 256, 0, s>>>(a);
+  ffn_kernel<RF, SF, 2, MAXMF, PF><<<slots * nb2, WAVES * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -11,19 +11,22 @@
 
 namespace moe {
 
-// ---- tiling of the expert-grouped GEMMs (bf16 MFMA 32x32x16) -------------
-// A block is 4 wave64s.  It owns up to BM rows of one expert's group and
-// BN_WAVE columns per wave:
-//   stage 1 (gate/up): each wave owns 32 h columns = 32 gate rows + 32 up rows
-//                      of W1, so a block makes 128 h columns;
-//   stage 2 (down):    each wave owns 64 output columns, a block 256.
+// ---- tiling of the expert-grouped GEMMs (MFMA 16x16x32) ----------------
+// A block is 4 wave64s.  It owns up to BM rows of one expert's group; each
+// wave owns one run of 64 weight rows:
+//   stage 1 (gate/up): 32 h columns = 32 gate rows + 32 up rows of W1, so a
+//                      block makes 128 h columns;
+//   stage 2 (down):    64 output columns, a block 256.
 // K advances in chunks of KC; one chunk of one wave's 64 weight rows is a
-// "wave tile", stored contiguously in the blob.
-constexpr int BM = 96;           // rows of an expert group per row tile (6 x 16)
-constexpr int KC = 64;           // K per chunk (4 MFMA K-steps of 16)
-constexpr int WAVES = 4;         // waves per GEMM block
-constexpr int H_COLS_BLOCK = 128;  // stage-1 h columns per block
-constexpr int OUT_COLS_BLOCK = 256;  // stage-2 output columns per block
+// "wave tile", stored contiguously in the blob; the blob orders wave tiles by
+// run index, then K chunk, independent of the block shape.
+constexpr int BM = 96;             // rows of an expert group per row tile (6 x 16)
+constexpr int KC = 64;             // K per chunk (2 MFMA K-steps of 32)
+constexpr int WAVES = 4;           // waves per GEMM block
+constexpr int H_COLS_WAVE = 32;    // stage-1 h columns per wave run
+constexpr int OUT_COLS_WAVE = 64;  // stage-2 output columns per wave run
+constexpr int H_COLS_BLOCK = 128;    // the layer's ffn widths are multiples of this
+constexpr int OUT_COLS_BLOCK = 256;  // the layer's hidden width is a multiple of this
 
 // wave-tile bytes (64 weight rows x 64 K) per stored format
 constexpr int TILE_BYTES_BF16 = 64 * 64 * 2;        // 8192
@@ -66,6 +69,8 @@ struct WsLayout {
   size_t tiles;        // int2  [routed_slots]  (expert, first row) per tile
   size_t h_routed;     // act-typed [T*k, F]    intermediate h, permuted rows
   size_t h_shared;     // act-typed [T, Fs]     intermediate h of the shared expert
+  size_t x16;          // fp16 [T, d]           activations scaled by 2^-xexp[t] (int4 path)
+  size_t xexp;         // float [T]             2^xexp[t], the scale to undo
   size_t total;
 };
 
@@ -84,6 +89,9 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 8);
   L.h_routed = off; off = align256(off + (size_t)n * D.ffn * elem);
   L.h_shared = off; off = align256(off + (D.n_shared ? (size_t)T * D.shared_ffn * elem : 0));
+  const bool x16 = D.act == MOE_BF16 && D.expert_w == MOE_I4_G32;
+  L.x16 = off;      off = align256(off + (x16 ? (size_t)T * D.d * 2 : 0));
+  L.xexp = off;     off = align256(off + (x16 ? (size_t)T * 4 : 0));
   L.total = off;
   return L;
 }
@@ -112,6 +120,8 @@ struct FfnArgs {
   const uint8_t* shared_blob;
   void* h_routed;
   void* h_shared;
+  uint16_t* x16;    // fp16 activations of the int4 path (workspace)
+  float* xscale;    // per-token power of two undone in the gate/up epilogue
   float* out_assign;
   float* shared_out;
 };
