@@ -59,6 +59,8 @@ moe_status check_desc(const moe_desc* D) {
     if (D->d % OUT_COLS_BLOCK || D->ffn % H_COLS_BLOCK ||
         (D->n_shared && D->shared_ffn % H_COLS_BLOCK))
       return fail(MOE_EUNSUPPORTED, "BF16 path needs d %% 256 == 0 and ffn, shared_ffn %% 128 == 0");
+    if (D->expert_w == MOE_I4_G32 && D->ffn % (KC * LEAD_I4))
+      return fail(MOE_EUNSUPPORTED, "I4_G32 routed experts need ffn %% %d == 0", KC * LEAD_I4);
   } else {
     return fail(MOE_EUNSUPPORTED, "act dtype %d unsupported", D->act);
   }

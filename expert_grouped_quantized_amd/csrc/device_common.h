@@ -91,25 +91,6 @@ __device__ __forceinline__ uint32_t and_or_b32(uint32_t x, uint32_t m, uint32_t 
   return r;
 }
 
-// Signed bytes (0,1) or (2,3) of a dword as two fp16 values (exact): each
-// SDWA convert sign-extends one byte and writes one half of the result.
-__device__ __forceinline__ uint32_t sbytes01_f16x2(uint32_t x) {
-  uint32_t r;
-  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0"
-      : "=v"(r) : "v"(x));
-  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
-      : "+v"(r) : "v"(x));
-  return r;
-}
-__device__ __forceinline__ uint32_t sbytes23_f16x2(uint32_t x) {
-  uint32_t r;
-  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2"
-      : "=v"(r) : "v"(x));
-  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
-      : "+v"(r) : "v"(x));
-  return r;
-}
-
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 }  // namespace moe

@@ -131,9 +131,22 @@ struct WTile<MOE_I8_ROW> {
     r[3] = pack_bf16x2(sbyte2_f(w1), sbyte3_f(w1));
     return r;
   }
+  // fp16(code), exact: flipping a byte's sign bit gives code + 128 in
+  // [0, 255]; a byte permute sets it under the fp16 exponent byte 0x64, which
+  // reads as 1024 + code + 128, and one packed subtract of 1152 leaves the
+  // code.  (All compiler-visible ops: the MFMA that reads the result right
+  // after gets its hazard wait states.)
   __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t, uint32_t) const {
-    const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
-    return u32x4_t{sbytes01_f16x2(w0), sbytes23_f16x2(w0), sbytes01_f16x2(w1), sbytes23_f16x2(w1)};
+    const uint32_t w0 = v[f][2 * s] ^ 0x80808080u, w1 = v[f][2 * s + 1] ^ 0x80808080u;
+    const uint32_t hi = 0x64646464u;
+    const f16x2_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    // selector bytes 4..7 pick bytes of the first operand, 0..3 of the second
+    auto half2 = [&](uint32_t w, uint32_t sel) {
+      return __builtin_bit_cast(uint32_t,
+                                __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(w, hi, sel)) + off);
+    };
+    return u32x4_t{half2(w0, 0x00050004u), half2(w0, 0x00070006u), half2(w1, 0x00050004u),
+                   half2(w1, 0x00070006u)};
   }
 };
 
@@ -164,18 +177,20 @@ struct TileCtx {
   const uint16_t* arow[3];
 };
 
-template <int FMT, int STAGE, int MAXMF, int PF_MAX, int NMF, bool F16, bool NT>
+template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
 __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm,
                                           const TileCtx& C) {
-  // a bf16 wave tile is 4x the bytes (and registers) of an int4 one
-  constexpr int PF = FMT == MOE_BF16 ? 2 : PF_MAX;
+  constexpr int NMF = MAXMF;
+  // Lead of the loads, in K chunks: 4 for int4 weights (the bytes of the
+  // call); 2 for bf16 tiles (4x the bytes and registers of an int4 tile) and
+  // int8 shared tiles (re-read from cache by every row tile).
+  constexpr int PF = FMT == MOE_I4_G32 ? PF_MAX : LEAD_WIDE;
   constexpr int ROWS = MAXMF * 16;
   constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
   constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
   const int tid = threadIdx.x, lane = tid & 63;
   const int nk = C.nk;
   const size_t tb = tile_bytes(FMT);
-  const int c8 = tid & 7;
 
   f32x4_t acc[NMF][4];
 #pragma unroll
@@ -183,22 +198,28 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
 #pragma unroll
     for (int f = 0; f < 4; f++) acc[i][f] = f32x4_t{0, 0, 0, 0};
 
-  // A chunks are prefetched two ahead: chunk c travels in register set c & 1,
-  // then lands in LDS buffer c & 1.  Weight chunks are prefetched PF ahead in a
-  // ring of registers.  PF is even, so every index below is a compile-time one.
-  u32x4_t areg[2][PPT];
+  // Chunk c of the activations travels in register set c % PF, then lands in
+  // LDS buffer c & 1; chunk c of the weights sits in ring slot c % PF.
+  u32x4_t areg[PF][PPT];
   auto load_a = [&](int kc, u32x4_t (&dst)[PPT]) {
 #pragma unroll
-    for (int j = 0; j < PPT; j++)
-      dst[j] = C.arow[j] ? *(const u32x4_t*)(C.arow[j] + kc * KC) : u32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < PPT; j++) dst[j] = *(const u32x4_t*)(C.arow[j] + kc * KC);
   };
+  // Thread tid stages pieces (tid + 256 j) mod PIECES: in small tiles some
+  // pieces are stored twice (same bytes, same place), so no store sits
+  // behind a branch.
   auto store_a = [&](uint16_t* dst, const u32x4_t (&src)[PPT]) {
 #pragma unroll
-    for (int j = 0; j < PPT; j++)
-      if (tid + WAVES * 64 * j < PIECES)
-        *(u32x4_t*)(dst + lds_a_index((tid >> 3) + 8 * WAVES * j, c8)) = src[j];
+    for (int j = 0; j < PPT; j++) {
+      const int q = (tid + WAVES * 64 * j) % PIECES;
+      *(u32x4_t*)(dst + lds_a_index(q >> 3, q & 7)) = src[j];
+    }
   };
   const uint32_t nib_mask = 0x000f000fu, f16_magic = 0x64006400u;
+  // One chunk on all MAXMF row fragments.  Fragments past the tile's last row
+  // hold copies of its first row and are never stored: a straight-line run of
+  // MFMAs with no branch beats skipping them (a scalar branch per fragment
+  // breaks the MFMA issue stream).
   auto compute = [&](const uint16_t* as, const WTile<FMT>& w) {
 #pragma unroll
     for (int s = 0; s < 2; s++) {
@@ -209,39 +230,51 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
         av[i] = *(const u32x4_t*)(as + lds_a_index(i * 16 + (lane & 15), ch));
 #pragma unroll
       for (int f = 0; f < 4; f++) {
-        if (F16) {
-          const u32x4_t b = w.frag16(f, s, nib_mask, f16_magic);
+        const u32x4_t b = F16 ? w.frag16(f, s, nib_mask, f16_magic) : w.frag(f, s);
 #pragma unroll
-          for (int i = 0; i < NMF; i++) acc[i][f] = mfma16x16_f16(av[i], b, acc[i][f]);
-        } else {
-          const u32x4_t b = w.frag(f, s);
-#pragma unroll
-          for (int i = 0; i < NMF; i++) acc[i][f] = mfma16x16(av[i], b, acc[i][f]);
-        }
+        for (int i = 0; i < NMF; i++)
+          acc[i][f] = F16 ? mfma16x16_f16(av[i], b, acc[i][f]) : mfma16x16(av[i], b, acc[i][f]);
       }
     }
   };
 
-  static_assert(PF % 2 == 0, "weight prefetch depth must be even");
+  // The loop is peeled so that no load sits behind a condition: step kc
+  // issues the activation and weight loads of chunk kc + PF, in the order
+  // they will be waited for.  The memory counter retires loads in issue
+  // order, so a wait then covers the chunk it needs and nothing issued after
+  // it, and PF chunks stay in flight.  nk is a multiple of PF (the ABI's width
+  // checks).
+  static_assert(PF == 2 || PF == 4, "load lead must be 2 or 4 chunks");
   WTile<FMT> ring[PF];
+  const uint8_t* wnext = C.wt;
 #pragma unroll
-  for (int p = 0; p < PF; p++)
-    if (p < nk) ring[p].template load<NT>(C.wt + (size_t)p * tb, lane);
-  load_a(0, areg[0]);
-  if (1 < nk) load_a(1, areg[1]);
+  for (int p = 0; p < PF; p++) {
+    load_a(p, areg[p]);
+    ring[p].template load<NT>(wnext, lane);
+    wnext += tb;
+  }
   store_a(sm.a[0], areg[0]);
   __syncthreads();
-  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
+  for (int kc0 = 0; kc0 < nk - PF; kc0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; p++) {
-      const int kc = kc0 + p;
-      if (kc < nk) {  // block-uniform
-        if (kc + 2 < nk) load_a(kc + 2, areg[p & 1]);
-        compute(sm.a[p & 1], ring[p]);
-        if (kc + PF < nk) ring[p].template load<NT>(C.wt + (size_t)(kc + PF) * tb, lane);
-        if (kc + 1 < nk) store_a(sm.a[(p + 1) & 1], areg[(p + 1) & 1]);
-        __syncthreads();
-      }
+      load_a(kc0 + p + PF, areg[p]);  // set p held chunk kc0 + p, already in LDS
+      compute(sm.a[p & 1], ring[p]);
+      ring[p].template load<NT>(wnext, lane);
+      wnext += tb;
+      store_a(sm.a[(p + 1) & 1], areg[(p + 1) % PF]);
+      __syncthreads();
+      // keep the scheduler from hoisting the next chunk's dequantization
+      // into this one (it would hold two chunks' registers at once)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; p++) {  // the last PF chunks: nothing more to load
+    compute(sm.a[p & 1], ring[p]);
+    if (p + 1 < PF) {
+      store_a(sm.a[(p + 1) & 1], areg[p + 1]);
+      __syncthreads();
     }
   }
 
@@ -349,23 +382,16 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
   const uint16_t* abase = STAGE == 1 ? (F16 ? (const uint16_t*)A.x16 : (const uint16_t*)A.hidden)
                                      : (const uint16_t*)(J.shared ? A.h_shared : A.h_routed);
   const size_t astride = STAGE == 1 ? (size_t)A.d : (size_t)C.Fw;
+  // Rows past the tile's end load the tile's first row: their accumulator
+  // rows are never stored, and every lane issues the same loads.
 #pragma unroll
-  for (int j = 0; j < 3; j++) {
-    const int r = (tid >> 3) + 8 * WAVES * j;  // piece tid + 64*WAVES*j: row r, 16-byte chunk tid % 8
-    const int s = (j < PPT && tid + WAVES * 64 * j < PIECES) ? sm.src[r] : -1;
-    C.arow[j] = s >= 0 ? abase + (size_t)s * astride + (tid & 7) * 8 : nullptr;
+  for (int j = 0; j < PPT; j++) {
+    const int q = (tid + WAVES * 64 * j) % PIECES;  // piece q: row q / 8, 16-byte chunk q % 8
+    const int r = q >> 3;
+    const int s = sm.src[r] >= 0 ? sm.src[r] : sm.src[0];
+    C.arow[j] = abase + (size_t)s * astride + (q & 7) * 8;
   }
-  // the number of live 16-row fragments is a compile-time constant of the
-  // loop, so every step issues its A reads together and runs branch-free
-  const int nmf = (J.cnt + 15) >> 4;
-  switch (nmf) {
-    case 1: tile_body<FMT, STAGE, MAXMF, PF_MAX, 1, F16, NT>(A, J, sm, C); break;
-    case 2: if constexpr (MAXMF >= 2) tile_body<FMT, STAGE, MAXMF, PF_MAX, 2, F16, NT>(A, J, sm, C); break;
-    case 3: if constexpr (MAXMF >= 3) tile_body<FMT, STAGE, MAXMF, PF_MAX, 3, F16, NT>(A, J, sm, C); break;
-    case 4: if constexpr (MAXMF >= 4) tile_body<FMT, STAGE, MAXMF, PF_MAX, 4, F16, NT>(A, J, sm, C); break;
-    case 5: if constexpr (MAXMF >= 5) tile_body<FMT, STAGE, MAXMF, PF_MAX, 5, F16, NT>(A, J, sm, C); break;
-    default: if constexpr (MAXMF >= 6) tile_body<FMT, STAGE, MAXMF, PF_MAX, MAXMF, F16, NT>(A, J, sm, C); break;
-  }
+  tile_body<FMT, STAGE, MAXMF, PF_MAX, F16, NT>(A, J, sm, C);
 }
 
 // Grid: slot-major with the column block fastest *within an XCD*: block b runs
@@ -488,9 +514,9 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
 
 template <int RF, int SF>
 static hipError_t launch_pair(const FfnArgs& a, hipStream_t s) {
-  if (a.T <= 16) return launch_stages<RF, SF, 1, 4>(a, s);
-  if (a.T <= 32) return launch_stages<RF, SF, 2, 4>(a, s);
-  return launch_stages<RF, SF, BM / 16, 4>(a, s);
+  if (a.T <= 16) return launch_stages<RF, SF, 1, LEAD_I4>(a, s);
+  if (a.T <= 32) return launch_stages<RF, SF, 2, LEAD_I4>(a, s);
+  return launch_stages<RF, SF, BM / 16, LEAD_I4>(a, s);
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {

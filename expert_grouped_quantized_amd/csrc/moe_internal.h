@@ -27,6 +27,10 @@ constexpr int H_COLS_WAVE = 32;    // stage-1 h columns per wave run
 constexpr int OUT_COLS_WAVE = 64;  // stage-2 output columns per wave run
 constexpr int H_COLS_BLOCK = 128;    // the layer's ffn widths are multiples of this
 constexpr int OUT_COLS_BLOCK = 256;  // the layer's hidden width is a multiple of this
+// K chunks each wave keeps in flight: int4 weight tiles, and the wider bf16
+// and int8 ones.  A matrix's K must be a multiple of KC times its lead.
+constexpr int LEAD_I4 = 4;
+constexpr int LEAD_WIDE = 2;
 
 // wave-tile bytes (64 weight rows x 64 K) per stored format
 constexpr int TILE_BYTES_BF16 = 64 * 64 * 2;        // 8192

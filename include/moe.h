@@ -83,7 +83,8 @@ typedef enum moe_blob_kind {
  *   act MOE_BF16: expert_w MOE_BF16 or MOE_I4_G32,
  *                 shared_w MOE_BF16 or MOE_I8_ROW  (router bf16, y bf16)
  * Sizes: 1 <= n_experts <= 1024; n_shared 0 or 1.  For act MOE_BF16:
- * d % 256 == 0, ffn % 128 == 0, shared_ffn % 128 == 0.  For act MOE_F32:
+ * d % 256 == 0, ffn % 128 == 0 (% 256 with I4_G32 routed weights),
+ * shared_ffn % 128 == 0.  For act MOE_F32:
  * d, ffn, shared_ffn multiples of 64.  d, ffn, shared_ffn <= 16384.         */
 typedef struct moe_desc {
   int32_t d;          /* hidden width                                       */

@@ -53,6 +53,7 @@ def _route(desc, T=4, k=10, hidden=FAKE, rw=FAKE, bias=None, logits=FAKE, ids=FA
     (dict(n_shared=2), M.MOE_EINVAL, "n_shared"),
     (dict(d=2500), M.MOE_EUNSUPPORTED, "d % 256"),
     (dict(ffn=1000), M.MOE_EUNSUPPORTED, "ffn"),
+    (dict(ffn=1152), M.MOE_EUNSUPPORTED, "I4_G32 routed experts need ffn % 256"),
     (dict(act="i4g32"), M.MOE_EUNSUPPORTED, "act"),
     (dict(expert_w="i8row"), M.MOE_EUNSUPPORTED, "routed"),
     (dict(shared_w="i4g32"), M.MOE_EUNSUPPORTED, "shared"),
@@ -149,7 +150,7 @@ def _rand_expert(fmt, rows, K, n, rng):
                                           ("f32", "f32", 0), ("f32", "f32", 1)])
 def test_pack_unpack_roundtrip(act, fmt, kind):
     rng = np.random.default_rng(hash((act, fmt, kind)) % 2**32)
-    d, F, E = (256, 128, 3) if act == "bf16" else (128, 64, 2)
+    d, F, E = (256, 256, 3) if act == "bf16" else (128, 64, 2)
     desc = M.make_desc(d, E, F, 1, F, act=act, expert_w=fmt if kind == 0 else act,
                        shared_w=fmt if kind == 1 else act)
     n = E if kind == 0 else 1
@@ -171,13 +172,13 @@ def test_pack_unpack_roundtrip(act, fmt, kind):
 
 
 def test_pack_rejects_int4_minus_eight():
-    desc = M.make_desc(256, 1, 128, 0, 0, act="bf16", expert_w="i4g32")
-    q = np.zeros((1, 128, 256), np.int8)
+    desc = M.make_desc(256, 1, 256, 0, 0, act="bf16", expert_w="i4g32")
+    q = np.zeros((1, 256, 256), np.int8)
     q[0, 5, 7] = -8
     g = W.pack_int4(q)
-    s = np.full((1, 128, 8), 0x3C00, np.uint16)
-    dq = W.pack_int4(np.zeros((1, 256, 128), np.int8))
-    dsc = np.full((1, 256, 4), 0x3C00, np.uint16)
+    s = np.full((1, 256, 8), 0x3C00, np.uint16)
+    dq = W.pack_int4(np.zeros((1, 256, 256), np.int8))
+    dsc = np.full((1, 256, 8), 0x3C00, np.uint16)
     blob = np.empty(M.moe_blob_bytes(desc, 0), np.uint8)
     with pytest.raises(M.MoeError) as ei:
         M.moe_pack_experts(desc, 0, g, s, g, s, dq, dsc, blob)

@@ -51,18 +51,20 @@ def _sample(T, n, seed, extra=()):
 # ------------------------------------------------------------ small edge cases
 
 def _small_cfg(name, idx, **kw):
-    base = dict(T=300, d=256, E=16, k=4, F=128, n_shared=1, Fs=256, act=W.BF16, router=W.BF16,
+    base = dict(T=300, d=256, E=16, k=4, F=256, n_shared=1, Fs=256, act=W.BF16, router=W.BF16,
                 expert=W.I4G32, shared=W.I8ROW)
     base.update(kw)
     return W.LayerConfig(name, 100 + idx, **base)
 
 
 @pytest.mark.parametrize("cfg", [
-    _small_cfg("ragged_i4", 0),
-    _small_cfg("ragged_bf16", 1, expert=W.BF16, shared=W.BF16, T=257),
-    _small_cfg("mixed_i4_bf16shared", 2, shared=W.BF16, T=129),
-    _small_cfg("bf16_i8shared", 3, expert=W.BF16, T=77),
+    _small_cfg("ragged_i4", 0, d=512),
+    _small_cfg("ragged_bf16", 1, expert=W.BF16, shared=W.BF16, T=257, F=128, Fs=384),
+    _small_cfg("mixed_i4_bf16shared", 2, shared=W.BF16, T=129, F=512, Fs=384),
+    _small_cfg("bf16_i8shared", 3, expert=W.BF16, T=77, F=384, Fs=128),
     _small_cfg("T1", 4, T=1),
+    _small_cfg("T5_i8shared", 11, T=5),        # one-fragment tiles, int8 shared on fp16 MFMA
+    _small_cfg("T20_i8shared", 12, T=20),      # two-fragment tiles
     _small_cfg("E1_k1_dense", 5, E=1, k=1, n_shared=0, Fs=0, T=200),
     _small_cfg("k32_E64", 6, E=64, k=32, T=40),
     _small_cfg("wide_E1024", 7, E=1024, k=8, T=96, n_shared=0, Fs=0),
