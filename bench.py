@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
     p.add_argument("--workload", choices=("both", "prefill", "decode"), default="both",

@@ -18,9 +18,8 @@ namespace moe {
 //    operands are read straight from global memory in MFMA fragment order
 //    (16x16x32: lane l holds row l%16, K elements 8*(l/16)..+7), and the 8
 //    partial 16x16 tiles are summed through LDS in a fixed wave order.
-//  * large T: a block owns 64 tokens x 256 experts; the token rows are staged
-//    through LDS (double-buffered, next chunk prefetched into registers) and
-//    each wave streams its 64 router rows straight into MFMA registers.
+//  * large T: a block owns 64 tokens x 128 experts; token rows and router
+//    rows are both staged through LDS with four chunks of loads in flight.
 
 typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
@@ -86,90 +85,102 @@ __global__ __launch_bounds__(RS_WAVES * 64) void router_small_kernel(
   }
 }
 
-constexpr int RL_M = 64, RL_N = 256;
+constexpr int RL_M = 64, RL_N = 128, RL_LEAD = 4;
 
-__global__ __launch_bounds__(256, 2) void router_large_kernel(int T, int d, int E,
+// Large T: a block owns 64 tokens x 128 experts; each of its 4 waves makes
+// 64 tokens x 32 experts.  Token rows and router rows are both staged through
+// LDS, 64 K at a time, double-buffered; every thread keeps RL_LEAD chunks of
+// its staging loads in flight (issued in the order they are waited for, no
+// load behind a condition).  Rows past T or E read row T-1 / E-1 and are
+// never stored.  Grid: the expert blocks of one token block share an XCD
+// (block b runs on XCD b % 8), so its L2 holds their common token rows.
+__global__ __launch_bounds__(256, 2) void router_large_kernel(int T, int d, int E, int neb,
+                                                              int ntb,
                                                               const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ wr,
                                                               const float* __restrict__ bias,
                                                               float* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][RL_M * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][RL_N * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * RL_M, n0 = blockIdx.x * RL_N + wave * 64;
-  // A staging: 64 rows x 8 chunks of 16 B = 512 pieces, 2 per thread
-  const int c8 = tid & 7;
-  const uint16_t* arow[2];
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int tb = (j / neb) * 8 + xcd, eb = j % neb;
+  if (tb >= ntb) return;
+  const int m0 = tb * RL_M, n0 = eb * RL_N;
+  // staging pieces (16 B): A 64 rows x 8 = 512 -> 2 per thread, B 128 x 8 -> 4
+  const int c8 = tid & 7, r0 = tid >> 3;
+  const uint16_t* ap[2];
+  const uint16_t* bp[4];
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int r = (tid >> 3) + 32 * j;
-    arow[j] = m0 + r < T ? x + (size_t)(m0 + r) * d + c8 * 8 : nullptr;
-  }
-  // B: wave's 64 experts = 2 fragments of 32; lane l holds expert row l%32
-  const uint16_t* brow[2];
+  for (int q = 0; q < 2; q++) ap[q] = x + (size_t)min(m0 + r0 + 32 * q, T - 1) * d + c8 * 8;
 #pragma unroll
-  for (int f = 0; f < 2; f++) {
-    const int e = n0 + f * 32 + (lane & 31);
-    brow[f] = e < E ? wr + (size_t)e * d + 8 * (lane >> 5) : nullptr;
-  }
-  const u32x4_t zero = {0, 0, 0, 0};
-  f32x16_t acc[2][2];
+  for (int q = 0; q < 4; q++) bp[q] = wr + (size_t)min(n0 + r0 + 32 * q, E - 1) * d + c8 * 8;
+  u32x4_t ar[RL_LEAD][2], br[RL_LEAD][4];
+  auto load = [&](int kc, u32x4_t (&a)[2], u32x4_t (&bb)[4]) {
 #pragma unroll
-  for (int i = 0; i < 2; i++) acc[i][0] = acc[i][1] = f32x16_t{};
-  u32x4_t areg[2], b[2][4], bn[2][4];
-  auto load_a = [&](int kc) {
+    for (int q = 0; q < 2; q++) a[q] = *(const u32x4_t*)(ap[q] + kc * 64);
 #pragma unroll
-    for (int j = 0; j < 2; j++) areg[j] = arow[j] ? *(const u32x4_t*)(arow[j] + kc) : zero;
+    for (int q = 0; q < 4; q++) bb[q] = *(const u32x4_t*)(bp[q] + kc * 64);
   };
-  auto store_a = [&](uint16_t* dst) {
+  auto store = [&](int buf, const u32x4_t (&a)[2], const u32x4_t (&bb)[4]) {
 #pragma unroll
-    for (int j = 0; j < 2; j++) *(u32x4_t*)(dst + lds_a_index((tid >> 3) + 32 * j, c8)) = areg[j];
+    for (int q = 0; q < 2; q++) *(u32x4_t*)(As[buf] + lds_a_index(r0 + 32 * q, c8)) = a[q];
+#pragma unroll
+    for (int q = 0; q < 4; q++) *(u32x4_t*)(Bs[buf] + lds_a_index(r0 + 32 * q, c8)) = bb[q];
   };
-  auto load_b = [&](int kc, u32x4_t (&dst)[2][4]) {
+  f32x4_t acc[4][2];
 #pragma unroll
-    for (int f = 0; f < 2; f++)
+  for (int i = 0; i < 4; i++) acc[i][0] = acc[i][1] = f32x4_t{0, 0, 0, 0};
+  auto compute = [&](int buf) {
 #pragma unroll
-      for (int s = 0; s < 4; s++) dst[f][s] = brow[f] ? *(const u32x4_t*)(brow[f] + kc + s * 16) : zero;
-  };
-  auto compute = [&](const uint16_t* as, const u32x4_t (&bb)[2][4]) {
+    for (int s = 0; s < 2; s++) {
+      const int ch = 4 * s + (lane >> 4);
+      u32x4_t bv[2];
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
+      for (int f = 0; f < 2; f++)
+        bv[f] = *(const u32x4_t*)(Bs[buf] + lds_a_index(wave * 32 + f * 16 + (lane & 15), ch));
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const u32x4_t av = *(const u32x4_t*)(as + lds_a_index(i * 32 + (lane & 31), 2 * s + (lane >> 5)));
-        acc[i][0] = mfma32(av, bb[0][s], acc[i][0]);
-        acc[i][1] = mfma32(av, bb[1][s], acc[i][1]);
+      for (int i = 0; i < 4; i++) {
+        const u32x4_t av = *(const u32x4_t*)(As[buf] + lds_a_index(i * 16 + (lane & 15), ch));
+        acc[i][0] = mfma16(av, bv[0], acc[i][0]);
+        acc[i][1] = mfma16(av, bv[1], acc[i][1]);
       }
     }
   };
-  const int nk = d / 64;  // even (d % 256 == 0)
-  load_a(0);
-  load_b(0, b);
-  store_a(As[0]);
+  const int nk = d / 64;  // a multiple of RL_LEAD (d % 256 == 0)
+#pragma unroll
+  for (int p = 0; p < RL_LEAD; p++) load(p, ar[p], br[p]);
+  store(0, ar[0], br[0]);
   __syncthreads();
-  for (int kc = 0; kc < nk; kc += 2) {
-    load_a((kc + 1) * 64);
-    load_b((kc + 1) * 64, bn);
-    compute(As[0], b);
-    store_a(As[1]);
-    __syncthreads();
-    if (kc + 2 < nk) {
-      load_a((kc + 2) * 64);
-      load_b((kc + 2) * 64, b);
+  for (int kc0 = 0; kc0 < nk - RL_LEAD; kc0 += RL_LEAD) {
+#pragma unroll
+    for (int p = 0; p < RL_LEAD; p++) {
+      load(kc0 + p + RL_LEAD, ar[p], br[p]);  // set p held chunk kc0 + p, already in LDS
+      compute(p & 1);
+      store((p + 1) & 1, ar[(p + 1) % RL_LEAD], br[(p + 1) % RL_LEAD]);
+      __syncthreads();
     }
-    compute(As[1], bn);
-    if (kc + 2 < nk) store_a(As[0]);
-    __syncthreads();
   }
 #pragma unroll
+  for (int p = 0; p < RL_LEAD; p++) {
+    compute(p & 1);
+    if (p + 1 < RL_LEAD) {
+      store((p + 1) & 1, ar[p + 1], br[p + 1]);
+      __syncthreads();
+    }
+  }
+  // accumulator r of fragment (i, f): token i*16 + 4*(lane/16) + r, expert
+  // wave*32 + f*16 + lane%16
+#pragma unroll
   for (int f = 0; f < 2; f++) {
-    const int e = n0 + f * 32 + (lane & 31);
+    const int e = n0 + wave * 32 + f * 16 + (lane & 15);
     if (e >= E) continue;
     const float bv = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < 4; i++) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int t = m0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int r = 0; r < 4; r++) {
+        const int t = m0 + i * 16 + 4 * (lane >> 4) + r;
         if (t < T) logits[(size_t)t * E + e] = acc[i][f][r] + bv;
       }
     }
@@ -203,9 +214,11 @@ hipError_t launch_router_bf16(int T, int d, int E, const void* x, const void* wr
     router_small_kernel<2><<<nb, th, 0, s>>>(T, d, E, xp, wp, bias, logits);
   else if (T <= 64)
     router_small_kernel<4><<<nb, th, 0, s>>>(T, d, E, xp, wp, bias, logits);
-  else
-    router_large_kernel<<<dim3((E + RL_N - 1) / RL_N, (T + RL_M - 1) / RL_M), 256, 0, s>>>(
-        T, d, E, xp, wp, bias, logits);
+  else {
+    const int neb = (E + RL_N - 1) / RL_N, ntb = (T + RL_M - 1) / RL_M;
+    const int blocks = (ntb + 7) / 8 * 8 * neb;
+    router_large_kernel<<<blocks, 256, 0, s>>>(T, d, E, neb, ntb, xp, wp, bias, logits);
+  }
   return hipGetLastError();
 }
 
