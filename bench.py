@@ -121,9 +121,11 @@ def algorithmic(cfg, T, n_active):
     shared = 3 * d * Fs * wbytes[cfg.shared] + (2 * Fs + d) * 2 * (cfg.shared == "i8row")
     weight_bytes = n_active * per_expert + shared
     act = T * d * 2 * 2 + E * d * 2                     # x in, y out, router weights
-    inter = T * k * F * 2 * 2 + T * Fs * 2 * 2 + T * k * d * 4 * 2 + T * d * 4 * 2
+    # h (bf16) written and read back; per-assignment and shared outputs (bf16)
+    # written by the down products and read by the combine
+    inter = T * k * F * 2 * 2 + T * Fs * 2 * 2 + T * k * d * 2 * 2 + T * d * 2 * 2
     return dict(ffn_flops=ffn_flops, router_flops=router_flops, weight_bytes=weight_bytes,
-                ffn_bytes=weight_bytes + T * d * 2 + inter - T * d * 4 - T * k * d * 4,
+                ffn_bytes=weight_bytes + T * d * 2 + inter - T * d * 2 - T * k * d * 2,
                 layer_bytes=weight_bytes + act + inter)
 
 
@@ -147,6 +149,25 @@ def cpu_baseline(cfg, inp: dict, T: int, n_tok: int):
                       f"(fp64 router, top-k, per-expert SwiGLU, shared expert, sum); {dt:.1f} s"}
 
 
+def counted_traffic(workload: str):
+    """HBM bytes per moe_grouped_ffn launch from the committed rocprofv3 counter
+    runs (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE, each scaled by
+    what it reads for a 1 GiB copy), or None once the GEMM kernel sources have
+    changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "moe_internal.h", "device_common.h"):
+        with open(os.path.join(ROOT, "expert_grouped_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("src_sha256") != h.hexdigest() or workload not in rec:
+        return None
+    return rec[workload]["grouped_ffn_bytes_per_launch"]
+
+
 def run_prefill(args, torch, W):
     """The T=4096 prefill workload; returns (result dict, roofline dict, host inputs)."""
     cfg = W.CONFIGS["int4_T4096"]
@@ -166,7 +187,7 @@ def run_prefill(args, torch, W):
                layer_gbs=A["layer_bytes"] / (ms_per_step * 1e-3) / 1e9)
     roof = {"bound": "mfma", "kernel": "moe_grouped_ffn (gate/up + down GEMMs)",
             "achieved": round(ffn_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ffn_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(ffn_tflops / BF16_PEAK_TFLOPS, 4), "traffic": counted_traffic("prefill"),
             "algorithmic_flops_per_launch": A["ffn_flops"], "avg_launch_ms": round(ffn_ms, 4)}
     inputs = S.inputs
     del S
@@ -191,7 +212,7 @@ def run_decode(args, torch, W):
                ffn_weight_gbs=ffn_gbs)
     roof = {"bound": "hbm", "kernel": "moe_grouped_ffn (gate/up + down weight streams)",
             "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic("decode"),
             "algorithmic_bytes_per_launch": DA["weight_bytes"], "avg_launch_ms": round(dper[2], 4)}
     del D
     torch.cuda.empty_cache()

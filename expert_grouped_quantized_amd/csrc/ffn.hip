@@ -279,7 +279,26 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
   }
 
   // ---- epilogue.  Accumulator r of fragment (i, f) is row i*16 + 4*(lane/16)
-  // + r and column 16*f + lane%16 of the wave's 64 weight rows.
+  // + r and column 16*f + lane%16 of the wave's 64 weight rows.  Results are
+  // stored as bf16 two columns at a time: lanes l and l^1 (columns c, c+1)
+  // trade values through DPP, the even lane writes rows r = 0, 1 of the pair
+  // and the odd lane rows 2, 3, each as one 4-byte store.
+  const bool odd = lane & 1;
+  auto store_pairs = [&](uint16_t* base, size_t ld, int col, int mrow, const float (&v)[4]) {
+    // base: row 0 of this tile; col: this lane's column; mrow: row of v[0]
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int r = odd ? 2 + q : q;  // the row this lane writes
+      // each lane sends the value its partner needs: the even lane row 2+q,
+      // the odd lane row q (quad_perm [1,0,3,2] swaps neighbours)
+      const float other = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, odd ? v[q] : v[2 + q]), 0xB1,
+                                          0xF, 0xF, false));
+      const uint32_t w = odd ? pack_bf16x2(other, v[r]) : pack_bf16x2(v[r], other);
+      if (mrow + r < J.cnt)
+        *(uint32_t*)(base + (size_t)(mrow + r) * ld + (col & ~1)) = w;
+    }
+  };
   const int Fw = C.Fw;
   const uint16_t* rscale =
       FMT == MOE_I8_ROW
@@ -297,34 +316,31 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       }
 #pragma unroll
       for (int i = 0; i < NMF; i++) {
+        float hv[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
           const int m = i * 16 + 4 * (lane >> 4) + r;
-          if (m < J.cnt) {
-            float g = acc[i][f][r] * sg, u = acc[i][f + 2][r] * su;
-            if (F16) {
-              g *= sm.xs[m];
-              u *= sm.xs[m];
-            }
-            const float h = sm.wrow[m] * silu_fast(g) * u;
-            hout[(size_t)(J.start + m) * Fw + col] = (uint16_t)(pack_bf16x2(h, 0.0f) & 0xffffu);
+          float g = acc[i][f][r] * sg, u = acc[i][f + 2][r] * su;
+          if (F16) {
+            g *= sm.xs[m];
+            u *= sm.xs[m];
           }
+          hv[r] = sm.wrow[m] * silu_fast(g) * u;
         }
+        store_pairs(hout + (size_t)J.start * Fw, Fw, col, i * 16 + 4 * (lane >> 4), hv);
       }
     }
   } else {
-    float* out = J.shared ? A.shared_out : A.out_assign;
+    uint16_t* out = (uint16_t*)(J.shared ? A.shared_out : A.out_assign);
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       const int col = C.run * OUT_COLS_WAVE + f * 16 + (lane & 15);
       const float sc = FMT == MOE_I8_ROW ? f16_bits_to_f32(rscale[col]) : 1.0f;
 #pragma unroll
       for (int i = 0; i < NMF; i++) {
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int m = i * 16 + 4 * (lane >> 4) + r;
-          if (m < J.cnt) out[(size_t)(J.start + m) * A.d + col] = acc[i][f][r] * sc;
-        }
+        const float ov[4] = {acc[i][f][0] * sc, acc[i][f][1] * sc, acc[i][f][2] * sc,
+                             acc[i][f][3] * sc};
+        store_pairs(out + (size_t)J.start * A.d, A.d, col, i * 16 + 4 * (lane >> 4), ov);
       }
     }
   }
@@ -572,7 +588,7 @@ __global__ __launch_bounds__(64) void ffn_f32_stage2(FfnArgs A, int NB) {
                                               : A.routed_blob + (size_t)J.expert * expert_bytes(MOE_F32, A.d, A.F));
   const float* wd = blob + (size_t)2 * Fw * A.d + (size_t)n * Fw;
   const float* H = (const float*)(J.shared ? A.h_shared : A.h_routed);
-  float* out = J.shared ? A.shared_out : A.out_assign;
+  float* out = (float*)(J.shared ? A.shared_out : A.out_assign);
   for (int m = 0; m < J.cnt; m++) {
     const float* h = H + (size_t)(J.start + m) * Fw;
     float o = 0.0f;
