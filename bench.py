@@ -121,11 +121,11 @@ def algorithmic(cfg, T, n_active):
     shared = 3 * d * Fs * wbytes[cfg.shared] + (2 * Fs + d) * 2 * (cfg.shared == "i8row")
     weight_bytes = n_active * per_expert + shared
     act = T * d * 2 * 2 + E * d * 2                     # x in, y out, router weights
-    # h (bf16) written and read back; per-assignment and shared outputs (bf16)
+    # h (bf16) written and read back; per-assignment and shared outputs (fp32)
     # written by the down products and read by the combine
-    inter = T * k * F * 2 * 2 + T * Fs * 2 * 2 + T * k * d * 2 * 2 + T * d * 2 * 2
+    inter = T * k * F * 2 * 2 + T * Fs * 2 * 2 + T * k * d * 4 * 2 + T * d * 4 * 2
     return dict(ffn_flops=ffn_flops, router_flops=router_flops, weight_bytes=weight_bytes,
-                ffn_bytes=weight_bytes + T * d * 2 + inter - T * d * 2 - T * k * d * 2,
+                ffn_bytes=weight_bytes + T * d * 2 + inter - T * d * 4 - T * k * d * 4,
                 layer_bytes=weight_bytes + act + inter)
 
 

@@ -428,8 +428,8 @@ moe_status moe_permute(const moe_desc* D, int32_t T, int32_t k, const int32_t* t
 
 moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
-                           const void* routed_blob, const void* shared_blob, void* out_assign,
-                           void* shared_out, void* workspace, size_t ws_bytes, void* stream) {
+                           const void* routed_blob, const void* shared_blob, float* out_assign,
+                           float* shared_out, void* workspace, size_t ws_bytes, void* stream) {
   TRY(check_desc(D));
   TRY(check_tk(D, T, k));
   TRY(check_ptr(hidden, "hidden"));
@@ -469,8 +469,8 @@ moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* 
                        "grouped-ffn launch");
 }
 
-moe_status moe_combine(const moe_desc* D, int32_t T, int32_t k, const void* out_assign,
-                       const int32_t* inv_perm, const void* shared_out, void* y, void* stream) {
+moe_status moe_combine(const moe_desc* D, int32_t T, int32_t k, const float* out_assign,
+                       const int32_t* inv_perm, const float* shared_out, void* y, void* stream) {
   TRY(check_desc(D));
   TRY(check_tk(D, T, k));
   TRY(check_ptr(out_assign, "out_assign"));

@@ -280,11 +280,11 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
 
   // ---- epilogue.  Accumulator r of fragment (i, f) is row i*16 + 4*(lane/16)
   // + r and column 16*f + lane%16 of the wave's 64 weight rows.  Results are
-  // stored as bf16 two columns at a time: lanes l and l^1 (columns c, c+1)
-  // trade values through DPP, the even lane writes rows r = 0, 1 of the pair
-  // and the odd lane rows 2, 3, each as one 4-byte store.
+  // stored two columns at a time: lanes l and l^1 (columns c, c+1) trade
+  // values through DPP, the even lane writes rows r = 0, 1 of the pair and
+  // the odd lane rows 2, 3, each as one store (bf16 h: 4 bytes, fp32: 8).
   const bool odd = lane & 1;
-  auto store_pairs = [&](uint16_t* base, size_t ld, int col, int mrow, const float (&v)[4]) {
+  auto store_pairs = [&](auto* base, size_t ld, int col, int mrow, const float (&v)[4]) {
     // base: row 0 of this tile; col: this lane's column; mrow: row of v[0]
 #pragma unroll
     for (int q = 0; q < 2; q++) {
@@ -294,9 +294,14 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       const float other = __builtin_bit_cast(
           float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, odd ? v[q] : v[2 + q]), 0xB1,
                                           0xF, 0xF, false));
-      const uint32_t w = odd ? pack_bf16x2(other, v[r]) : pack_bf16x2(v[r], other);
-      if (mrow + r < J.cnt)
-        *(uint32_t*)(base + (size_t)(mrow + r) * ld + (col & ~1)) = w;
+      const float lo = odd ? other : v[r], hi = odd ? v[r] : other;
+      auto* dst = base + (size_t)(mrow + r) * ld + (col & ~1);
+      if (mrow + r < J.cnt) {
+        if constexpr (sizeof(*base) == 2)
+          *(uint32_t*)dst = pack_bf16x2(lo, hi);
+        else
+          *(float2*)dst = make_float2(lo, hi);
+      }
     }
   };
   const int Fw = C.Fw;
@@ -331,7 +336,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       }
     }
   } else {
-    uint16_t* out = (uint16_t*)(J.shared ? A.shared_out : A.out_assign);
+    float* out = J.shared ? A.shared_out : A.out_assign;
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       const int col = C.run * OUT_COLS_WAVE + f * 16 + (lane & 15);
@@ -588,7 +593,7 @@ __global__ __launch_bounds__(64) void ffn_f32_stage2(FfnArgs A, int NB) {
                                               : A.routed_blob + (size_t)J.expert * expert_bytes(MOE_F32, A.d, A.F));
   const float* wd = blob + (size_t)2 * Fw * A.d + (size_t)n * Fw;
   const float* H = (const float*)(J.shared ? A.h_shared : A.h_routed);
-  float* out = (float*)(J.shared ? A.shared_out : A.out_assign);
+  float* out = J.shared ? A.shared_out : A.out_assign;
   for (int m = 0; m < J.cnt; m++) {
     const float* h = H + (size_t)(J.start + m) * Fw;
     float o = 0.0f;

@@ -126,13 +126,13 @@ struct FfnArgs {
   void* h_shared;
   uint16_t* x16;    // fp16 activations of the int4 path (workspace)
   float* xscale;    // per-token power of two undone in the gate/up epilogue
-  void* out_assign;  // activation dtype: bf16 (GEMM path) or fp32 (fp32 path)
-  void* shared_out;
+  float* out_assign;
+  float* shared_out;
 };
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
-hipError_t launch_combine(int T, int k, int d, int act, const void* out_assign,
-                          const int32_t* inv_perm, const void* shared_out, void* y,
+hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,
+                          const int32_t* inv_perm, const float* shared_out, void* y,
                           hipStream_t s);
 
 }  // namespace moe

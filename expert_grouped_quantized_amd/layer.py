@@ -33,8 +33,8 @@ class MoELayer:
         self.offsets = z((E + 1,), i32)
         self.perm = z((max(n, 1),), i32)
         self.inv_perm = z((max(n, 1),), i32)
-        self.out_assign = z((max(n, 1), d), act)
-        self.shared_out = z((max(T_max, 1), d), act) if desc.n_shared else None
+        self.out_assign = z((max(n, 1), d), f32)
+        self.shared_out = z((max(T_max, 1), d), f32) if desc.n_shared else None
         self.y = z((max(T_max, 1), d), act)
         self.ws_bytes = moe_workspace_bytes(desc, T_max, k)
         self.workspace = z((self.ws_bytes,), torch.uint8)

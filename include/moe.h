@@ -173,17 +173,16 @@ moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const int32_t
  * expert e and each p in [offsets[e], offsets[e+1]), with f = perm[p],
  * t = f / k and weight w = topk_w[f]:
  *   h = w * silu(Wg_e x_t) (.) (Wu_e x_t)        (router weight folded in)
- *   out_assign[p] = Wd_e h                       one row per assignment
+ *   out_assign[p] = Wd_e h                       fp32, one row per assignment
  * and for the shared expert (n_shared == 1), every token t:
- *   shared_out[t] = Wd_s (silu(Wg_s x_t) (.) (Wu_s x_t))
+ *   shared_out[t] = Wd_s (silu(Wg_s x_t) (.) (Wu_s x_t))   fp32
  *   hidden      [T, d] act dtype
  *   topk_w      [T*k] fp32 (from moe_route)
  *   offsets, perm        from moe_permute
  *   routed_blob, shared_blob  device copies of moe_pack_experts blobs
  *             (shared_blob NULL iff n_shared == 0)
- *   out_assign  [T*k, d] act dtype out (bf16 or fp32), in permuted order
- *               (row p)
- *   shared_out  [T, d] act dtype out (NULL iff n_shared == 0)
+ *   out_assign  [T*k, d] fp32 out, in permuted order (row p)
+ *   shared_out  [T, d] fp32 out (NULL iff n_shared == 0)
  *   workspace   the workspace moe_permute filled (holds its tile plan and the
  *               intermediate h).
  * Arithmetic (act BF16): MFMA with fp32 accumulation.  bf16 weights run bf16
@@ -192,24 +191,22 @@ moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const int32_t
  * magnitude lies in [2^14, 2^15) (undone on the fp32 accumulator); int4
  * weights become fp16(code * scale) there and bf16(code * scale) in the
  * down product; int8 codes enter exactly, their row scale applied to the
- * fp32 accumulator.  h and the outputs are rounded to bf16 (nearest even).
- * The fp32 path computes and stores in fp32 throughout.                     */
+ * fp32 accumulator.  h is rounded to bf16 (nearest even); the outputs stay
+ * fp32.  The fp32 path computes and stores in fp32 throughout.              */
 moe_status moe_grouped_ffn(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
-                           const void* routed_blob, const void* shared_blob, void* out_assign,
-                           void* shared_out, void* workspace, size_t workspace_bytes,
+                           const void* routed_blob, const void* shared_blob, float* out_assign,
+                           float* shared_out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
 /* Fixed-order combine ("Dedicated prefill lane", step 5), no atomics:
  *   y[t] = act( ((out_assign[inv_perm[t*k+0]] + ... ) + out_assign[inv_perm[t*k+k-1]])
  *               + shared_out[t] )
- * each term widened to fp32 and summed in fp32 in exactly that order, then
- * rounded to the act dtype (bf16: round to nearest even).  out_assign and
- * shared_out are in the act dtype, as moe_grouped_ffn writes them; shared_out
- * may be NULL (n_shared == 0).
+ * summed in fp32 in exactly that order, then rounded to the act dtype (bf16:
+ * round to nearest even).  shared_out may be NULL (n_shared == 0).
  *   y [T, d] act dtype out.                                                 */
-moe_status moe_combine(const moe_desc* desc, int32_t T, int32_t k, const void* out_assign,
-                       const int32_t* inv_perm, const void* shared_out, void* y, void* stream);
+moe_status moe_combine(const moe_desc* desc, int32_t T, int32_t k, const float* out_assign,
+                       const int32_t* inv_perm, const float* shared_out, void* y, void* stream);
 
 #ifdef __cplusplus
 }

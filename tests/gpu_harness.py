@@ -54,8 +54,8 @@ class GpuLayer:
         out = dict(logits=cpu(L.logits[:T]), ids=cpu(L.ids[:n]).reshape(T, self.cfg.k),
                    w=cpu(L.w[:n]).reshape(T, self.cfg.k), offsets=cpu(L.offsets),
                    perm=cpu(L.perm[:n]), inv_perm=cpu(L.inv_perm[:n]),
-                   out_assign=cpu(L.out_assign[:n].float()),
-                   shared_out=cpu(L.shared_out[:T].float()) if self.cfg.n_shared else None)
+                   out_assign=cpu(L.out_assign[:n]),
+                   shared_out=cpu(L.shared_out[:T]) if self.cfg.n_shared else None)
         if self.cfg.act == W.BF16:
             out["y"] = y.float().cpu().numpy()
             out["y_bits"] = y.view(torch.int16).cpu().numpy()
