@@ -20,7 +20,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_harness import (GpuLayer, check_plan, check_route, check_values,  # noqa: E402
+from gpu_harness import (GpuLayer, check_plan, check_route, check_values, rel_l2, spec_of,  # noqa: E402
                          desc_of)
 
 
@@ -117,6 +117,37 @@ def test_integer_exact_logits_and_ties():
     ids_o, w_o = check_route(cfg, inp, out)
     check_plan(cfg, out)
     check_values(cfg, inp, out, w_o)
+
+
+def test_activation_rows_over_a_wide_range():
+    """int4 layers run gate/up on fp16 MFMA, each token row scaled by its own
+    power of two.  Rows scaled by 2^-40 .. 2^40, an all-zero row and rows with
+    one outlier 2^20 above the rest must each match the oracle on their own
+    scale (a shared or missing scale would flush small rows or overflow big
+    ones), and the zero row must give exactly zero."""
+    cfg = _small_cfg("range", 13, T=96, k=4)
+    inp = W.generate(cfg)
+    x = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    rng = np.random.default_rng(13)
+    exps = rng.integers(-40, 41, size=cfg.T)
+    x *= np.exp2(exps)[:, None]
+    x[7] = 0.0
+    for t in (11, 12, 13):
+        x[t] *= 2.0 ** -10
+        x[t, rng.integers(cfg.d)] = 2.0 ** 10
+    inp["x"] = W.to_bf16_bits(x.astype(np.float32))
+    g = GpuLayer(cfg, inp)
+    out = g.run(inp["x"])
+    ids_o, w_o = check_route(cfg, inp, out)
+    check_plan(cfg, out)
+    y_ref, _, _ = oracle.moe_experts(spec_of(cfg), inp, out["ids"], w_o)
+    assert not out["y"][7].any(), "the zero row must stay exactly zero"
+    for t in range(cfg.T):
+        if t == 7:
+            continue
+        r = rel_l2(out["y"][t], y_ref[t])
+        assert r <= 5e-3, f"row {t} (scale 2^{exps[t]}): rel-L2 {r:.3e}"
+    _say("[ok] range", f"worst row rel-L2 {max(rel_l2(out['y'][t], y_ref[t]) for t in range(cfg.T) if t != 7):.2e}")
 
 
 def test_route_from_logits_signed_zero_and_ties():
