@@ -445,6 +445,13 @@ __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_r
 // column blocks of a matrix with `runs` 64-row weight runs
 __host__ __device__ __forceinline__ int col_blocks(int runs) { return (runs + WAVES - 1) / WAVES; }
 
+// Gate/up of int4 layers runs fp16 MFMA on the fp16 copy of x: its int4 ->
+// fp16 conversion costs fewer VALU ops than bf16, which sets the speed of the
+// large-T loop and still shows in the weight-streaming small-T one.
+__host__ __device__ constexpr bool x16_path(int routed_fmt, int) {
+  return routed_fmt == MOE_I4_G32;
+}
+
 template <int RF, int SF, int STAGE, int MAXMF, int PF>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   __shared__ __attribute__((aligned(16))) Smem<MAXMF> sm;
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   if (!decode_job(A, max(nr, ns), nr, ns, MAXMF * 16, J)) return;
   // int4 routed layers run gate/up on fp16 MFMA (the fp16 activation copy
   // exists); int8 shared tiles of such a layer follow; bf16 weights stay bf16
-  constexpr bool X16 = RF == MOE_I4_G32;
+  constexpr bool X16 = x16_path(RF, MAXMF);
   // Routed weights of a small-T call are read exactly once: stream them.  The
   // shared expert's weights are re-read by every row tile, and a prefill
   // expert can span two tiles: keep those cacheable.
@@ -520,7 +527,7 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
   const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
   const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
-  if (RF == MOE_I4_G32) {
+  if (x16_path(RF, MAXMF)) {
     x_to_f16_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.T, a.d, (const uint16_t*)a.hidden, a.x16,
                                                    a.xscale);
     hipError_t e = hipGetLastError();
