@@ -43,6 +43,12 @@ __device__ __forceinline__ u32x4_t ldw(const uint8_t* base, int i) {
   return ((const u32x4_t*)base)[i];
 }
 
+// Constants of the int4 -> fp16 conversion, kept in registers (VOP3
+// encodings take no literal operands).
+struct F16Consts {
+  uint32_t lo, hi, magic;
+};
+
 // ---- weight registers of one wave tile (64 rows x 64 K) -------------------
 // Fragment f (0..3) is 16 weight rows; step s (0..1) is 32 K.  Lane l holds
 // row l % 16 of each fragment and K elements 32*s + 8*(l/16) .. +7.
@@ -59,7 +65,8 @@ struct WTile<MOE_BF16> {
     for (int j = 0; j < 8; j++) v[j] = ldw<NT>(t, j * 64 + lane);
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s) const { return v[f * 2 + s]; }
-  __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t, uint32_t) const {
+  template <bool>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     return v[f * 2 + s];  // never used: bf16 weights run bf16 MFMA
   }
 };
@@ -98,17 +105,36 @@ struct WTile<MOE_I4_G32> {
   }
   // fp16(code * scale): a nibble pair OR-ed into two fp16 mantissas is
   // (1024 + code + 8) each; one packed subtract makes the codes exact, one
-  // packed multiply by the fp16 scale rounds each product to nearest even
-  __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t m, uint32_t o) const {
+  // packed multiply by the fp16 scale rounds each product to nearest even.
+  // ONE_SHIFT (used where registers are plentiful) takes the pairs held in
+  // the high nibbles of bytes 0 and 2 in place, as 1024 + 16 (code + 8), and
+  // makes them exact with one packed fma by 1/16 and -72 instead of a shift:
+  // one shift per dword instead of three, the same results bit for bit.
+  template <bool ONE_SHIFT>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts& k) const {
     const uint32_t sb = scale_bits(f, s);
     const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
     const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
     u32x4_t r;
+    if constexpr (ONE_SHIFT) {
+      const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+      const uint32_t q8 = q >> 8;
+      const f16x2_t t0 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.lo, k.magic));
+      const f16x2_t t1 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.hi, k.magic));
+      const f16x2_t t2 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.lo, k.magic));
+      const f16x2_t t3 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.hi, k.magic));
+      r[0] = __builtin_bit_cast(uint32_t, (t0 + off) * s2);
+      r[1] = __builtin_bit_cast(uint32_t, (t1 * sixteenth + off16) * s2);
+      r[2] = __builtin_bit_cast(uint32_t, (t2 + off) * s2);
+      r[3] = __builtin_bit_cast(uint32_t, (t3 * sixteenth + off16) * s2);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), m, o));
-      r[j] = __builtin_bit_cast(uint32_t, (t + off) * s2);
+      for (int j = 0; j < 4; j++) {
+        const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), k.lo, k.magic));
+        r[j] = __builtin_bit_cast(uint32_t, (t + off) * s2);
+      }
     }
     return r;
   }
@@ -136,7 +162,8 @@ struct WTile<MOE_I8_ROW> {
   // reads as 1024 + code + 128, and one packed subtract of 1152 leaves the
   // code.  (All compiler-visible ops: the MFMA that reads the result right
   // after gets its hazard wait states.)
-  __device__ __forceinline__ u32x4_t frag16(int f, int s, uint32_t, uint32_t) const {
+  template <bool>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     const uint32_t w0 = v[f][2 * s] ^ 0x80808080u, w1 = v[f][2 * s + 1] ^ 0x80808080u;
     const uint32_t hi = 0x64646464u;
     const f16x2_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
@@ -215,7 +242,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       *(u32x4_t*)(dst + lds_a_index(q >> 3, q & 7)) = src[j];
     }
   };
-  const uint32_t nib_mask = 0x000f000fu, f16_magic = 0x64006400u;
+  const F16Consts f16k = {0x000f000fu, 0x00f000f0u, 0x64006400u};
   // One chunk on all MAXMF row fragments.  Fragments past the tile's last row
   // hold copies of its first row and are never stored: a straight-line run of
   // MFMAs with no branch beats skipping them (a scalar branch per fragment
@@ -230,7 +257,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
         av[i] = *(const u32x4_t*)(as + lds_a_index(i * 16 + (lane & 15), ch));
 #pragma unroll
       for (int f = 0; f < 4; f++) {
-        const u32x4_t b = F16 ? w.frag16(f, s, nib_mask, f16_magic) : w.frag(f, s);
+        const u32x4_t b = F16 ? w.template frag16<(MAXMF <= 2)>(f, s, f16k) : w.frag(f, s);
 #pragma unroll
         for (int i = 0; i < NMF; i++)
           acc[i][f] = F16 ? mfma16x16_f16(av[i], b, acc[i][f]) : mfma16x16(av[i], b, acc[i][f]);
