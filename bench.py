@@ -111,6 +111,64 @@ def time_steps(S: Setup, steps: int, warmup: int):
     return wall, layer_ms, per_call
 
 
+def time_graph(S: Setup, steps: int):
+    """The four calls captured as one HIP graph per routed-blob copy, replayed
+    back to back; wall clock and HIP-event time per replay."""
+    torch = S.torch
+    graphs = []
+    for i in range(N_ROT):
+        S.layer.routed_blob = S.routed[i]
+        graphs.append(S.layer.capture(S.x, S.T))
+    for i in range(2 * N_ROT):
+        graphs[i % N_ROT].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        graphs[i % N_ROT].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graphs
+    return wall * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def measured_peaks(torch):
+    """Secondary denominators measured on this GPU: a large bf16 GEMM
+    (torch.mm, 8192^3, hipBLASLt) and a 2 GiB device-to-device copy (bytes
+    read + written per second)."""
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 2.0 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    src = torch.ones(1 << 31, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(tflops, 1), "hbm_copy_gbs": round(gbs, 1),
+            "how": "torch.mm bf16 8192^3; 2 GiB device-to-device copy, read + write bytes"}
+
+
 def algorithmic(cfg, T, n_active):
     """Flops and bytes of one layer call (the definition, not what the kernels move)."""
     d, F, Fs, k, E = cfg.d, cfg.F, cfg.Fs, cfg.k, cfg.E
@@ -214,7 +272,25 @@ def run_decode(args, torch, W):
             "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic("decode"),
             "algorithmic_bytes_per_launch": DA["weight_bytes"], "avg_launch_ms": round(dper[2], 4)}
+    # the same layer as one HIP graph per step, at 16 rows and at 32 rows (a
+    # verify batch): the 32-row call's cost against its byte ratio
+    g_ms, g_ev = time_graph(D, args.decode_steps)
+    res["graph"] = dict(ms_per_step=g_ms, event_ms_per_step=g_ev, tokens_per_s=16 / (g_ms * 1e-3),
+                        layer_hbm_frac=DA["layer_bytes"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
     del D
+    torch.cuda.empty_cache()
+    D32 = Setup(dcfg, 32, torch)
+    D32.step(0)
+    torch.cuda.synchronize()
+    a32 = int((np.diff(D32.layer.offsets.cpu().numpy()) > 0).sum())
+    g32_ms, g32_ev = time_graph(D32, args.decode_steps)
+    A32 = algorithmic(dcfg, 32, a32)
+    res["graph_T32"] = dict(ms_per_step=g32_ms, event_ms_per_step=g32_ev, active_experts=a32,
+                            tokens_per_s=32 / (g32_ms * 1e-3),
+                            layer_hbm_frac=A32["layer_bytes"] / (g32_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            time_ratio_to_T16=g32_ms / g_ms,
+                            byte_ratio_to_T16=A32["layer_bytes"] / DA["layer_bytes"])
+    del D32
     torch.cuda.empty_cache()
     return res, roof
 
@@ -247,6 +323,7 @@ def main():
         prefill, roof_p, pre_inputs = run_prefill(args, torch, W)
     if args.workload in ("both", "decode"):
         decode, roof_d = run_decode(args, torch, W)
+    peaks = measured_peaks(torch)
     cpu = None
     if not args.no_cpu_baseline and pre_inputs is not None:
         cfg = W.CONFIGS["int4_T4096"]
@@ -283,6 +360,11 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    line["measured_peaks"] = peaks
+    if roof_p is not None:
+        roof_p["frac_of_measured_peak"] = round(roof_p["achieved"] / peaks["mfma_bf16_tflops"], 4)
+    if roof_d is not None:
+        roof_d["frac_of_measured_peak"] = round(roof_d["achieved"] / peaks["hbm_copy_gbs"], 4)
     if prefill is not None:
         line["prefill"] = _r(prefill)
     if decode is not None:

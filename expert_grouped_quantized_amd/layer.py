@@ -71,6 +71,19 @@ class MoELayer:
         self.combine(T)
         return self.y[:T]
 
+    def capture(self, x, T=None):
+        """Record the four calls on x (a static device buffer) into one HIP
+        graph; replaying it reruns the layer on whatever x then holds, with the
+        weights bound at capture time.  Returns the torch graph object."""
+        import torch
+        T = x.shape[0] if T is None else T
+        self.forward(x, T)  # warm: first launches of each kernel happen outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, T)
+        return g
+
 
 def blobs_from_inputs(desc, inputs: dict):
     """Pack the routed (and shared) expert blobs of a workloads.generate() dict."""

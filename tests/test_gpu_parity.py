@@ -150,6 +150,34 @@ def test_activation_rows_over_a_wide_range():
     _say("[ok] range", f"worst row rel-L2 {max(rel_l2(out['y'][t], y_ref[t]) for t in range(cfg.T) if t != 7):.2e}")
 
 
+@pytest.mark.parametrize("T", [16, 40])
+def test_graph_replay_matches_eager(T):
+    """The four calls captured as one HIP graph: every replay, with eager calls
+    on another input between the replays, equals the eager result bit for bit
+    (no call records a memset; every buffer is the caller's)."""
+    cfg = _small_cfg(f"graph{T}", 14, T=T)
+    inp = W.generate(cfg)
+    g = GpuLayer(cfg, inp)
+    x_a = inp["x"]
+    x_b = W.to_bf16_bits(W.bf16_bits_to_f32(x_a)[::-1].copy() * 0.5)
+    y_a = g.run(x_a)["y_bits"].copy()
+    y_b = g.run(x_b)["y_bits"].copy()
+    assert not np.array_equal(y_a, y_b)
+    static = g.x_tensor(x_a).clone()
+    graph = g.layer.capture(static, T)
+    L = g.layer
+    for i in range(3):
+        static.copy_(g.x_tensor(x_a))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(L.y[:T].view(torch.int16).cpu().numpy(), y_a), f"replay {i} (a)"
+        assert np.array_equal(g.run(x_b)["y_bits"], y_b), f"eager {i} (b)"
+        static.copy_(g.x_tensor(x_b))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(L.y[:T].view(torch.int16).cpu().numpy(), y_b), f"replay {i} (b)"
+
+
 def test_route_from_logits_signed_zero_and_ties():
     import expert_grouped_quantized_amd as M
     E, k, T = 512, 10, 64
