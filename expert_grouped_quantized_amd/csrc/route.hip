@@ -88,7 +88,10 @@ __global__ __launch_bounds__(RS_WAVES * 64) void router_small_kernel(
 constexpr int RL_M = 64, RL_N = 128, RL_LEAD = 4;
 
 // Large T: a block owns 64 tokens x 128 experts; each of its 4 waves makes
-// 64 tokens x 32 experts.  Token rows and router rows are both staged through
+// 64 tokens x 32 experts.  A logit is summed exactly as the small-T kernel
+// sums it -- K in eight equal slices, each an MFMA chain from zero in
+// ascending K, the slices then added in slice order -- so a token's logits,
+// and hence its routing, do not depend on how many tokens share the call.  Token rows and router rows are both staged through
 // LDS, 64 K at a time, double-buffered; every thread keeps RL_LEAD chunks of
 // its staging loads in flight (issued in the order they are waited for, no
 // load behind a condition).  Rows past T or E read row T-1 / E-1 and are
@@ -128,10 +131,12 @@ __global__ __launch_bounds__(256, 2) void router_large_kernel(int T, int d, int 
 #pragma unroll
     for (int q = 0; q < 4; q++) *(u32x4_t*)(Bs[buf] + lds_a_index(r0 + 32 * q, c8)) = bb[q];
   };
-  f32x4_t acc[4][2];
+  f32x4_t acc[4][2], tot[4][2];
 #pragma unroll
-  for (int i = 0; i < 4; i++) acc[i][0] = acc[i][1] = f32x4_t{0, 0, 0, 0};
-  auto compute = [&](int buf) {
+  for (int i = 0; i < 4; i++)
+    acc[i][0] = acc[i][1] = tot[i][0] = tot[i][1] = f32x4_t{0, 0, 0, 0};
+  const int slice_steps = d / (32 * RS_WAVES);  // 32-K steps per K slice
+  auto compute = [&](int buf, int kc) {
 #pragma unroll
     for (int s = 0; s < 2; s++) {
       const int ch = 4 * s + (lane >> 4);
@@ -145,6 +150,17 @@ __global__ __launch_bounds__(256, 2) void router_large_kernel(int T, int d, int 
         acc[i][0] = mfma16(av, bv[0], acc[i][0]);
         acc[i][1] = mfma16(av, bv[1], acc[i][1]);
       }
+      const int step = 2 * kc + s + 1;  // 32-K steps done
+      if (step % slice_steps == 0) {    // a K slice ends: fold it into the total (uniform branch)
+        const bool first = step == slice_steps;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int f = 0; f < 2; f++) {
+            tot[i][f] = first ? acc[i][f] : tot[i][f] + acc[i][f];
+            acc[i][f] = f32x4_t{0, 0, 0, 0};
+          }
+      }
     }
   };
   const int nk = d / 64;  // a multiple of RL_LEAD (d % 256 == 0)
@@ -156,14 +172,14 @@ __global__ __launch_bounds__(256, 2) void router_large_kernel(int T, int d, int 
 #pragma unroll
     for (int p = 0; p < RL_LEAD; p++) {
       load(kc0 + p + RL_LEAD, ar[p], br[p]);  // set p held chunk kc0 + p, already in LDS
-      compute(p & 1);
+      compute(p & 1, kc0 + p);
       store((p + 1) & 1, ar[(p + 1) % RL_LEAD], br[(p + 1) % RL_LEAD]);
       __syncthreads();
     }
   }
 #pragma unroll
   for (int p = 0; p < RL_LEAD; p++) {
-    compute(p & 1);
+    compute(p & 1, nk - RL_LEAD + p);
     if (p + 1 < RL_LEAD) {
       store((p + 1) & 1, ar[p + 1], br[p + 1]);
       __syncthreads();
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void router_large_kernel(int T, int d, int 
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int t = m0 + i * 16 + 4 * (lane >> 4) + r;
-        if (t < T) logits[(size_t)t * E + e] = acc[i][f][r] + bv;
+        if (t < T) logits[(size_t)t * E + e] = tot[i][f][r] + bv;
       }
     }
   }

@@ -178,6 +178,23 @@ def test_graph_replay_matches_eager(T):
         assert np.array_equal(L.y[:T].view(torch.int16).cpu().numpy(), y_b), f"replay {i} (b)"
 
 
+@pytest.mark.parametrize("expert,shared", [(W.I4G32, W.I8ROW), (W.BF16, W.BF16)])
+def test_rows_do_not_depend_on_the_batch(expert, shared):
+    """A token's logits and output bits are the same whichever kernels its
+    call size selects: 300 tokens (large-T router, 96-row tiles), 40 (small-T
+    router, 96-row tiles), 20 (32-row tiles) and 5 (16-row tiles), the smaller
+    calls taking the first rows of the largest."""
+    cfg = _small_cfg("rowinv", 15, T=300, expert=expert, shared=shared)
+    inp = W.generate(cfg)
+    g = GpuLayer(cfg, inp, T_max=300)
+    full = g.run(inp["x"])
+    for n in (40, 20, 5):
+        part = g.run(inp["x"][:n])
+        assert np.array_equal(part["logits"], full["logits"][:n]), f"T={n}: logits differ"
+        assert np.array_equal(part["ids"], full["ids"][:n]), f"T={n}: ids differ"
+        assert np.array_equal(part["y_bits"], full["y_bits"][:n]), f"T={n}: y differs"
+
+
 def test_route_from_logits_signed_zero_and_ties():
     import expert_grouped_quantized_amd as M
     E, k, T = 512, 10, 64
