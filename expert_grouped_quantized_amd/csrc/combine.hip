@@ -13,7 +13,8 @@ namespace moe {
 constexpr int COMBINE_COLS = 512;  // columns per block: 128 threads x 4
 
 // Block (t, c): token t, columns [c*512, c*512 + 512).  A thread's k slot
-// loads are issued eight at a time, then added in slot order.
+// loads are issued eight at a time, then added in slot order.  Every partial
+// is read exactly once: the loads are non-temporal.
 template <int ACT>
 __global__ __launch_bounds__(128) void combine_kernel(int k, int d,
                                                       const float* __restrict__ out_assign,
@@ -26,17 +27,17 @@ __global__ __launch_bounds__(128) void combine_kernel(int k, int d,
   if (threadIdx.x < k) rows[threadIdx.x] = inv_perm[(size_t)t * k + threadIdx.x];
   __syncthreads();
   if (c >= d) return;
-  f32x4_t acc = *(const f32x4_t*)(out_assign + (size_t)rows[0] * d + c);
+  f32x4_t acc = __builtin_nontemporal_load((const f32x4_t*)(out_assign + (size_t)rows[0] * d + c));
   int s = 1;
   for (; s + 8 <= k; s += 8) {
     f32x4_t v[8];
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = *(const f32x4_t*)(out_assign + (size_t)rows[s + j] * d + c);
+    for (int j = 0; j < 8; j++) v[j] = __builtin_nontemporal_load((const f32x4_t*)(out_assign + (size_t)rows[s + j] * d + c));
 #pragma unroll
     for (int j = 0; j < 8; j++) acc += v[j];
   }
-  for (; s < k; s++) acc += *(const f32x4_t*)(out_assign + (size_t)rows[s] * d + c);
-  if (shared_out) acc += *(const f32x4_t*)(shared_out + (size_t)t * d + c);
+  for (; s < k; s++) acc += __builtin_nontemporal_load((const f32x4_t*)(out_assign + (size_t)rows[s] * d + c));
+  if (shared_out) acc += __builtin_nontemporal_load((const f32x4_t*)(shared_out + (size_t)t * d + c));
   if (ACT == MOE_F32) {
     *(f32x4_t*)((float*)y + (size_t)t * d + c) = acc;
   } else {
