@@ -218,7 +218,7 @@ def counted_traffic(workload: str):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
-    for f in ("ffn.hip", "moe_internal.h", "device_common.h"):
+    for f in ("ffn.hip", "wave_tile.h", "moe_internal.h", "device_common.h"):
         with open(os.path.join(ROOT, "expert_grouped_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if rec.get("src_sha256") != h.hexdigest() or workload not in rec:

@@ -131,6 +131,8 @@ struct FfnArgs {
 };
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+// x -> fp16 copy and per-token scale (int4 layers)
+hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,
                           const int32_t* inv_perm, const float* shared_out, void* y,
                           hipStream_t s);

@@ -1,0 +1,267 @@
+// wave_tile.h -- one wave's share of an expert-grouped GEMM tile: the MFMA
+// wrappers, the weight-tile registers with their in-register dequantization,
+// and the epilogue that stores a wave's 64 weight rows x (16 * NMF) tile rows.
+// Kept apart from the kernels that use it so their row tiles of every size
+// share one arithmetic.
+#pragma once
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_f __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4_t mfma16x16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_f, a),
+                                                 __builtin_bit_cast(bf16x8_f, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16_f16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Weight loads; NT streams them past the caches (non-temporal) for weights that
+// one row tile reads once, so they do not evict activation rows.
+template <bool NT>
+__device__ __forceinline__ u32x4_t ldw(const uint8_t* base, int i) {
+  if (NT) return __builtin_nontemporal_load((const u32x4_t*)base + i);
+  return ((const u32x4_t*)base)[i];
+}
+
+// Constants of the int4 -> fp16 conversion, kept in registers (VOP3
+// encodings take no literal operands).
+struct F16Consts {
+  uint32_t lo, hi, magic;
+};
+
+// ---- weight registers of one wave tile (64 rows x 64 K) -------------------
+// Fragment f (0..3) is 16 weight rows; step s (0..1) is 32 K.  Lane l holds
+// row l % 16 of each fragment and K elements 32*s + 8*(l/16) .. +7.
+// frag() returns the 8 weights as bf16 (for bf16 MFMA), frag16() as fp16.
+template <int FMT>
+struct WTile;
+
+template <>
+struct WTile<MOE_BF16> {
+  u32x4_t v[8];  // [frag][step]
+  template <bool NT>
+  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = ldw<NT>(t, j * 64 + lane);
+  }
+  __device__ __forceinline__ u32x4_t frag(int f, int s) const { return v[f * 2 + s]; }
+  template <bool>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
+    return v[f * 2 + s];  // never used: bf16 weights run bf16 MFMA
+  }
+};
+
+template <>
+struct WTile<MOE_I4_G32> {
+  // [frag pair]; dword (f%2)*2 + s holds the lane's 8 codes + 8: element 2j in
+  // nibble j, element 2j+1 in nibble j+4 (so nibbles j and j+4, at bits 4j and
+  // 16+4j, are the pair that one packed fp16 register takes)
+  u32x4_t v[2];
+  u32x4_t sc;  // 8 fp16 group scales, index f*2 + s (group = step)
+  template <bool NT>
+  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+    v[0] = ldw<NT>(t, lane);
+    v[1] = ldw<NT>(t, 64 + lane);
+    sc = ldw<NT>(t + 2048, lane & 15);
+  }
+  __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
+    const int si = f * 2 + s;
+    const uint32_t sw = sc[si >> 1];
+    return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
+  }
+  // bf16(code * scale): code + 8 as a float, one FMA with the scale (exact in
+  // fp32), rounded to nearest even by the pack
+  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+    const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
+    const float bias = -8.0f * scale;
+    const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
+    const uint32_t lo = q & 0x0f0f0f0fu, hi = (q >> 4) & 0x0f0f0f0fu;
+    u32x4_t r;
+    r[0] = pack_bf16x2(fmaf(ubyte0_f(lo), scale, bias), fmaf(ubyte2_f(lo), scale, bias));
+    r[1] = pack_bf16x2(fmaf(ubyte0_f(hi), scale, bias), fmaf(ubyte2_f(hi), scale, bias));
+    r[2] = pack_bf16x2(fmaf(ubyte1_f(lo), scale, bias), fmaf(ubyte3_f(lo), scale, bias));
+    r[3] = pack_bf16x2(fmaf(ubyte1_f(hi), scale, bias), fmaf(ubyte3_f(hi), scale, bias));
+    return r;
+  }
+  // fp16(code * scale): a nibble pair OR-ed into two fp16 mantissas is
+  // (1024 + code + 8) each; one packed subtract makes the codes exact, one
+  // packed multiply by the fp16 scale rounds each product to nearest even.
+  // ONE_SHIFT (used where registers are plentiful) takes the pairs held in
+  // the high nibbles of bytes 0 and 2 in place, as 1024 + 16 (code + 8), and
+  // makes them exact with one packed fma by 1/16 and -72 instead of a shift:
+  // one shift per dword instead of three, the same results bit for bit.
+  template <bool ONE_SHIFT>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts& k) const {
+    const uint32_t sb = scale_bits(f, s);
+    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
+    const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
+    u32x4_t r;
+    if constexpr (ONE_SHIFT) {
+      const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+      const uint32_t q8 = q >> 8;
+      const f16x2_t t0 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.lo, k.magic));
+      const f16x2_t t1 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.hi, k.magic));
+      const f16x2_t t2 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.lo, k.magic));
+      const f16x2_t t3 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.hi, k.magic));
+      r[0] = __builtin_bit_cast(uint32_t, (t0 + off) * s2);
+      r[1] = __builtin_bit_cast(uint32_t, (t1 * sixteenth + off16) * s2);
+      r[2] = __builtin_bit_cast(uint32_t, (t2 + off) * s2);
+      r[3] = __builtin_bit_cast(uint32_t, (t3 * sixteenth + off16) * s2);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), k.lo, k.magic));
+        r[j] = __builtin_bit_cast(uint32_t, (t + off) * s2);
+      }
+    }
+    return r;
+  }
+};
+
+template <>
+struct WTile<MOE_I8_ROW> {
+  u32x4_t v[4];  // [frag]; dwords 2s, 2s+1 hold 8 int8 codes
+  template <bool NT>
+  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = ldw<NT>(t, j * 64 + lane);
+  }
+  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+    const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
+    u32x4_t r;
+    r[0] = pack_bf16x2(sbyte0_f(w0), sbyte1_f(w0));
+    r[1] = pack_bf16x2(sbyte2_f(w0), sbyte3_f(w0));
+    r[2] = pack_bf16x2(sbyte0_f(w1), sbyte1_f(w1));
+    r[3] = pack_bf16x2(sbyte2_f(w1), sbyte3_f(w1));
+    return r;
+  }
+  // fp16(code), exact: flipping a byte's sign bit gives code + 128 in
+  // [0, 255]; a byte permute sets it under the fp16 exponent byte 0x64, which
+  // reads as 1024 + code + 128, and one packed subtract of 1152 leaves the
+  // code.  (All compiler-visible ops: the MFMA that reads the result right
+  // after gets its hazard wait states.)
+  template <bool>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
+    const uint32_t w0 = v[f][2 * s] ^ 0x80808080u, w1 = v[f][2 * s + 1] ^ 0x80808080u;
+    const uint32_t hi = 0x64646464u;
+    const f16x2_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    // selector bytes 4..7 pick bytes of the first operand, 0..3 of the second
+    auto half2 = [&](uint32_t w, uint32_t sel) {
+      return __builtin_bit_cast(uint32_t,
+                                __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(w, hi, sel)) + off);
+    };
+    return u32x4_t{half2(w0, 0x00050004u), half2(w0, 0x00070006u), half2(w1, 0x00050004u),
+                   half2(w1, 0x00070006u)};
+  }
+};
+
+// Gate/up of int4 layers runs fp16 MFMA on the fp16 copy of x: its int4 ->
+// fp16 conversion costs fewer VALU ops than bf16, which sets the speed of the
+// large-T loop and still shows in the weight-streaming small-T one.
+__host__ __device__ constexpr bool x16_path(int routed_fmt, int) {
+  return routed_fmt == MOE_I4_G32;
+}
+
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Stores one wave's finished tile.  Accumulator r of fragment (i, f) is tile
+// row i*16 + 4*(lane/16) + r and column 16*f + lane%16 of the wave's 64
+// weight rows (run `run` of its matrix).
+//   stage 1: fragments 0,1 are gate rows and 2,3 the up rows of the same 32
+//            h columns; h = w * silu(g) * u in fp32, stored as bf16.  F16
+//            tiles ran on activations scaled by 1/xs(i, r): g and u are
+//            multiplied back first.  wrow(i, r) is the row's folded weight.
+//   stage 2: fp32 output rows.
+// int8 tiles apply their per-row fp16 scale here.  Values are stored two
+// columns at a time: lanes l and l^1 (columns c, c+1) trade values through
+// DPP, the even lane writes rows r = 0, 1 of the pair and the odd lane rows
+// 2, 3, each as one store (bf16: 4 bytes, fp32: 8).  Rows at or past `cnt`
+// are not stored.
+template <int FMT, int STAGE, int NMF, bool F16, typename RowW, typename RowS>
+__device__ __forceinline__ void store_wave_tile(const FfnArgs& A, bool shared, int start, int cnt,
+                                                int run, int Fw, const uint8_t* sect,
+                                                const f32x4_t (&acc)[NMF][4], RowW wrow,
+                                                RowS xs) {
+  const int lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
+  auto store_pairs = [&](auto* base, size_t ld, int col, int mrow, const float (&v)[4]) {
+    // base: row 0 of this tile; col: this lane's column; mrow: row of v[0]
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int r = odd ? 2 + q : q;  // the row this lane writes
+      // each lane sends the value its partner needs: the even lane row 2+q,
+      // the odd lane row q (quad_perm [1,0,3,2] swaps neighbours)
+      const float va = v[q], vb = v[2 + q];
+      const float other = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, odd ? va : vb), 0xB1, 0xF, 0xF,
+                                          false));
+      const float mine = odd ? vb : va;
+      const float lo = odd ? other : mine, hi = odd ? mine : other;
+      auto* dst = base + (size_t)(mrow + r) * ld + (col & ~1);
+      if (mrow + r < cnt) {
+        if constexpr (sizeof(*base) == 2)
+          *(uint32_t*)dst = pack_bf16x2(lo, hi);
+        else
+          *(float2*)dst = make_float2(lo, hi);
+      }
+    }
+  };
+  const size_t tb = tile_bytes(FMT);
+  const uint16_t* rscale =
+      FMT == MOE_I8_ROW
+          ? (const uint16_t*)(sect + (size_t)(STAGE == 1 ? (2 * Fw / 64) * (A.d / KC)
+                                                         : (A.d / 64) * (Fw / KC)) * tb)
+          : nullptr;
+  const int quad = 4 * (lane >> 4);
+  if (STAGE == 1) {
+    uint16_t* hout = (uint16_t*)(shared ? A.h_shared : A.h_routed);
+#pragma unroll
+    for (int f = 0; f < 2; f++) {
+      const int col = run * H_COLS_WAVE + f * 16 + (lane & 15);
+      float sg = 1.0f, su = 1.0f;
+      if (FMT == MOE_I8_ROW) {
+        sg = f16_bits_to_f32(rscale[col]);
+        su = f16_bits_to_f32(rscale[Fw + col]);
+      }
+#pragma unroll
+      for (int i = 0; i < NMF; i++) {
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          float g = acc[i][f][r] * sg, u = acc[i][f + 2][r] * su;
+          if (F16) {
+            g *= xs(i, r);
+            u *= xs(i, r);
+          }
+          hv[r] = wrow(i, r) * silu_fast(g) * u;
+        }
+        store_pairs(hout + (size_t)start * Fw, Fw, col, i * 16 + quad, hv);
+      }
+    }
+  } else {
+    float* out = shared ? A.shared_out : A.out_assign;
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+      const int col = run * OUT_COLS_WAVE + f * 16 + (lane & 15);
+      const float sc = FMT == MOE_I8_ROW ? f16_bits_to_f32(rscale[col]) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < NMF; i++) {
+        const float ov[4] = {acc[i][f][0] * sc, acc[i][f][1] * sc, acc[i][f][2] * sc,
+                             acc[i][f][3] * sc};
+        store_pairs(out + (size_t)start * A.d, A.d, col, i * 16 + quad, ov);
+      }
+    }
+  }
+}
+
+}  // namespace moe
