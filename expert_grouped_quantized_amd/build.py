@@ -1,36 +1,54 @@
-"""Compile the HIP library ``libmoe.so`` in-tree for gfx950 with hipcc."""
+"""Compile the HIP library ``libmoe.so`` in-tree for gfx950 with hipcc.
+
+Every source compiles to its own object in parallel, then one link."""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "ffn.hip", "combine.hip", "abi.cpp"]
-FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+SOURCES = ["route.hip", "permute.hip", "ffn.hip", "ffn_lowbit.hip", "combine.hip", "abi.cpp"]
+FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # keep the compiler from emitting packed-fp32 VALU instructions
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    """Build libmoe.so from every source (always recompiles)."""
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines()
             if "packed-fp32-ops" not in l and l.strip()]
-    if r.returncode != 0:
-        sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed ({r.returncode})")
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    return r.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Build libmoe.so from every source (always recompiles)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmp:
+        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+        cmds = [[hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_run, cmds))
+        for cmd, (rc, msgs) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if rc != 0:
+                sys.stderr.write("\n".join(msgs) + "\n")
+                raise RuntimeError(f"hipcc failed ({rc}) on {cmd[-3]}")
+            if verbose and msgs:
+                print("\n".join(msgs))
+        out = LIB + ".tmp"
+        rc, msgs = _run([hipcc, *FLAGS, "-shared", *objs, "-o", out])
+        if rc != 0:
+            sys.stderr.write("\n".join(msgs) + "\n")
+            raise RuntimeError(f"hipcc link failed ({rc})")
+    os.replace(out, LIB)
     return LIB
 
 

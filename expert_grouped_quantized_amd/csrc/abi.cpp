@@ -50,8 +50,9 @@ moe_status check_desc(const moe_desc* D) {
     if (D->d % 64 || D->ffn % 64 || (D->n_shared && D->shared_ffn % 64))
       return fail(MOE_EUNSUPPORTED, "F32 path needs d, ffn, shared_ffn multiples of 64");
   } else if (D->act == MOE_BF16) {
-    if (D->expert_w != MOE_BF16 && D->expert_w != MOE_I4_G32)
-      return fail(MOE_EUNSUPPORTED, "act BF16 needs routed weights BF16 or I4_G32 (got %d)",
+    if (D->expert_w != MOE_BF16 && ig32_bits(D->expert_w) == 0)
+      return fail(MOE_EUNSUPPORTED,
+                  "act BF16 needs routed weights BF16, I4_G32 or I{2,3,5,6,7,8}_G32 (got %d)",
                   D->expert_w);
     if (D->n_shared && D->shared_w != MOE_BF16 && D->shared_w != MOE_I8_ROW)
       return fail(MOE_EUNSUPPORTED, "act BF16 needs shared weights BF16 or I8_ROW (got %d)",
@@ -59,8 +60,9 @@ moe_status check_desc(const moe_desc* D) {
     if (D->d % OUT_COLS_BLOCK || D->ffn % H_COLS_BLOCK ||
         (D->n_shared && D->shared_ffn % H_COLS_BLOCK))
       return fail(MOE_EUNSUPPORTED, "BF16 path needs d %% 256 == 0 and ffn, shared_ffn %% 128 == 0");
-    if (D->expert_w == MOE_I4_G32 && D->ffn % (KC * LEAD_I4))
-      return fail(MOE_EUNSUPPORTED, "I4_G32 routed experts need ffn %% %d == 0", KC * LEAD_I4);
+    if (D->ffn % (KC * lead_of(D->expert_w, LEAD_I4)))
+      return fail(MOE_EUNSUPPORTED, "%d-bit routed experts need ffn %% %d == 0",
+                  ig32_bits(D->expert_w), KC * lead_of(D->expert_w, LEAD_I4));
   } else {
     return fail(MOE_EUNSUPPORTED, "act dtype %d unsupported", D->act);
   }
@@ -109,6 +111,13 @@ inline int i4_code(const MatIO& m, int64_t r, int64_t k) {
 }
 // nibble of a packed lane dword that holds element i (0..7) of the lane's 8
 inline int i4_nibble(int i) { return (i & 1) ? 4 + (i >> 1) : (i >> 1); }
+// b-bit group-32 tiles: byte offset of dword dw of lane `lane`'s code stream
+// (16-byte groups of all lanes, an odd b's last two dwords in 8-byte ones)
+inline size_t ig32_dword_offset(int b, int lane, int dw) {
+  const int G = (2 * b) / 4;
+  return dw < 4 * G ? (size_t)(dw >> 2) * 1024 + lane * 16 + (dw & 3) * 4
+                    : (size_t)G * 1024 + lane * 8 + (dw - 4 * G) * 4;
+}
 inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
   return ((const uint16_t*)m.s)[r * (m.K / 32) + k / 32];
 }
@@ -127,9 +136,45 @@ struct OutIO {  // canonical outputs of unpacking
   uint8_t* s;
 };
 
+// b-bit group-32 tile: lane l's codes of fragment f, K step s, as one bit
+// stream (code + 2^(b-1) at bit (2f + s) 8b + i b for element i), then the
+// fp16 group scales [row c][f][s] at 512 b + c*16.
+template <typename RowOf>
+bool pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
+  const int b = ig32_bits(m[0]->fmt), lim = (1 << (b - 1)) - 1;
+  for (int lane = 0; lane < 64; lane++) {
+    uint32_t w[17] = {0};  // one spare dword: a field may reach past the last
+    for (int f = 0; f < 4; f++) {
+      const MatIO& M = *m[f];
+      const int64_t r = row_of(f, lane & 15);
+      for (int s = 0; s < 2; s++) {
+        const int64_t k0 = kc * KC + s * 32 + 8 * (lane >> 4);
+        for (int i = 0; i < 8; i++) {
+          const int c = ((const int8_t*)M.q)[r * M.K + k0 + i];
+          if (c < -lim || c > lim) return false;
+          const uint64_t u = (uint64_t)(c + (1 << (b - 1)));
+          const int bit = (2 * f + s) * 8 * b + i * b;
+          const uint64_t cur = ((uint64_t)w[(bit >> 5) + 1] << 32) | w[bit >> 5];
+          const uint64_t nxt = cur | (u << (bit & 31));
+          w[bit >> 5] = (uint32_t)nxt;
+          w[(bit >> 5) + 1] = (uint32_t)(nxt >> 32);
+        }
+      }
+    }
+    for (int dw = 0; dw < 2 * b; dw++) memcpy(dst + ig32_dword_offset(b, lane, dw), &w[dw], 4);
+  }
+  for (int c = 0; c < 16; c++) {
+    uint16_t* o = (uint16_t*)(dst + 512 * b + c * 16);
+    for (int f = 0; f < 4; f++)
+      for (int s = 0; s < 2; s++) o[f * 2 + s] = i4_scale(*m[f], row_of(f, c), kc * KC + s * 32);
+  }
+  return true;
+}
+
 template <typename RowOf>
 bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   const int fmt = m[0]->fmt;
+  if (fmt != MOE_I4_G32 && ig32_bits(fmt) != 0) return pack_tile_ig32(m, row_of, kc, dst);
   for (int f = 0; f < 4; f++) {
     const MatIO& M = *m[f];
     for (int lane = 0; lane < 64; lane++) {
@@ -163,9 +208,38 @@ bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) 
 }
 
 template <typename RowOf>
+void unpack_tile_ig32(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int64_t kc,
+                      const uint8_t* src) {
+  const int b = ig32_bits(m[0]->fmt);
+  for (int lane = 0; lane < 64; lane++) {
+    uint32_t w[17] = {0};
+    for (int dw = 0; dw < 2 * b; dw++) memcpy(&w[dw], src + ig32_dword_offset(b, lane, dw), 4);
+    for (int f = 0; f < 4; f++) {
+      const int64_t r = row_of(f, lane & 15), K = m[f]->K;
+      for (int s = 0; s < 2; s++) {
+        const int64_t k0 = kc * KC + s * 32 + 8 * (lane >> 4);
+        for (int i = 0; i < 8; i++) {
+          const int bit = (2 * f + s) * 8 * b + i * b;
+          const uint64_t cur = ((uint64_t)w[(bit >> 5) + 1] << 32) | w[bit >> 5];
+          const int u = (int)((cur >> (bit & 31)) & ((1u << b) - 1));
+          ((int8_t*)out[f].q)[r * K + k0 + i] = (int8_t)(u - (1 << (b - 1)));
+        }
+      }
+    }
+  }
+  for (int c = 0; c < 16; c++) {
+    const uint16_t* o = (const uint16_t*)(src + 512 * b + c * 16);
+    for (int f = 0; f < 4; f++)
+      for (int s = 0; s < 2; s++)
+        ((uint16_t*)out[f].s)[row_of(f, c) * (m[f]->K / 32) + 2 * kc + s] = o[f * 2 + s];
+  }
+}
+
+template <typename RowOf>
 void unpack_tile(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int64_t kc,
                  const uint8_t* src) {
   const int fmt = m[0]->fmt;
+  if (fmt != MOE_I4_G32 && ig32_bits(fmt) != 0) return unpack_tile_ig32(m, out, row_of, kc, src);
   for (int f = 0; f < 4; f++) {
     const int64_t K = m[f]->K;
     for (int lane = 0; lane < 64; lane++) {
@@ -209,14 +283,15 @@ size_t canon_q_bytes(int fmt, int64_t rows, int64_t K) {
   }
 }
 size_t canon_s_bytes(int fmt, int64_t rows, int64_t K) {
-  return fmt == MOE_I4_G32 ? rows * (K / 32) * 2 : fmt == MOE_I8_ROW ? rows * 2 : 0;
+  return ig32_bits(fmt) ? rows * (K / 32) * 2 : fmt == MOE_I8_ROW ? rows * 2 : 0;
 }
 
 struct ExpertIO {  // canonical pointers of one expert (gate, up, down)
   const uint8_t *g, *gs, *u, *us, *dn, *ds;
 };
 
-// Pack (or, with unpack = true, unpack) one expert.  Returns false on a -8 code.
+// Pack (or, with unpack = true, unpack) one expert.  Returns false on a code
+// outside its format's symmetric range.
 bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool unpack) {
   const size_t w1b = w1_bytes(fmt, d, F);
   if (fmt == MOE_F32) {
@@ -297,7 +372,7 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
   const int64_t d = D->d, F = kind == MOE_BLOB_ROUTED ? D->ffn : D->shared_ffn;
   const size_t need = n * expert_bytes(fmt, d, F);
   if (!blob || !gate || !up || !down) return fail(MOE_EINVAL, "NULL weight or blob pointer");
-  if ((fmt == MOE_I4_G32 || fmt == MOE_I8_ROW) && (!gs || !us || !ds))
+  if ((ig32_bits(fmt) || fmt == MOE_I8_ROW) && (!gs || !us || !ds))
     return fail(MOE_EINVAL, "quantized weights need their scales");
   if (blob_bytes < need) return fail(MOE_EINVAL, "blob_bytes %zu < %zu", blob_bytes, need);
   const size_t gq = canon_q_bytes(fmt, F, d), gsb = canon_s_bytes(fmt, F, d);
@@ -317,7 +392,11 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
   for (int i = 0; i < nt; i++) th.emplace_back(work, n * i / nt, n * (i + 1) / nt);
   for (auto& t : th) t.join();
   for (int64_t e = 0; e < n; e++)
-    if (bad[e]) return fail(MOE_EINVAL, "expert %lld holds an int4 code -8 (codes must be in [-7, 7])", (long long)e);
+    if (bad[e]) {
+      const int b = ig32_bits(fmt);
+      return fail(MOE_EINVAL, "expert %lld holds a code outside [%d, %d]", (long long)e,
+                  -((1 << (b - 1)) - 1), (1 << (b - 1)) - 1);
+    }
   return ok();
 }
 

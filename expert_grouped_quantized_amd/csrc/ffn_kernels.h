@@ -1,0 +1,303 @@
+// ffn_kernels.h -- expert-grouped SwiGLU GEMMs ("Qwen3.8-Flash-Next-Dual-GPU"
+// README, section "Dedicated prefill lane", steps 2-4).
+//
+// Work unit: one row tile (up to BM = 96 consecutive rows of one expert's group
+// in the route plan, or up to 96 tokens of the always-active shared expert)
+// times one column block.  A block is 4 wave64s:
+//   stage 1: h[p] = w_p * silu(Wg x_t) (.) (Wu x_t)   -> h (bf16), rows p
+//            each wave owns 32 h columns: 32 gate rows and 32 up rows of W1
+//   stage 2: out[p] = Wd h[p]                          -> fp32, one row per
+//            assignment (out_assign) or per token (shared_out)
+//            each wave owns 64 output columns
+// Activations (x rows gathered through perm, or h rows) are staged through
+// LDS, 64 K at a time, double-buffered, and read as MFMA A operands by all 4
+// waves.  Weights stream straight from HBM into each wave's registers in the
+// tile order moe_pack_experts wrote them (one contiguous run per wave), PF
+// chunks ahead, are dequantized in registers to bf16 (int4: code * fp16 group
+// scale, rounded to nearest even; int8: the exact code, its row scale applied
+// to the fp32 accumulator), and feed bf16 MFMA 16x16x32 with fp32
+// accumulation.  A wave covers all rows of its tile, so each weight is read
+// and dequantized once per row tile; 16-row MFMA fragments past the tile's
+// last row are skipped.
+#pragma once
+
+#include "wave_tile.h"
+
+namespace moe {
+
+// ---- one (row tile, column block) ----------------------------------------
+struct TileJob {
+  bool shared;
+  int expert, start, cnt, nb;
+};
+
+template <int MAXMF>
+struct Smem {
+  uint16_t a[2][MAXMF * 16 * 64];
+  float wrow[MAXMF * 16];
+  float xs[MAXMF * 16];  // power of two to undo on fp16-staged rows
+  int src[MAXMF * 16];
+};
+
+// Per-tile constants shared by the setup and the main loop.
+struct TileCtx {
+  int Fw, nk;
+  int run;              // this wave's run of 64 weight rows
+  const uint8_t* sect;  // W1 or W2 section of this expert's blob
+  const uint8_t* wt;    // this wave's run of weight tiles
+  const uint16_t* arow[3];
+};
+
+template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
+__device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm,
+                                          const TileCtx& C) {
+  constexpr int NMF = MAXMF;
+  // Lead of the loads, in K chunks: 4 for int4 and 2-bit codes (the bytes of
+  // the call); 2 for bf16 tiles (4x the bytes and registers of an int4 tile),
+  // int8 shared tiles (re-read from cache by every row tile) and the 3- and
+  // 5- to 8-bit codes (their registers).
+  constexpr int PF = lead_of(FMT, PF_MAX);
+  constexpr int ROWS = MAXMF * 16;
+  constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
+  constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nk = C.nk;
+  const size_t tb = tile_bytes(FMT);
+
+  f32x4_t acc[NMF][4];
+#pragma unroll
+  for (int i = 0; i < NMF; i++)
+#pragma unroll
+    for (int f = 0; f < 4; f++) acc[i][f] = f32x4_t{0, 0, 0, 0};
+
+  // Chunk c of the activations travels in register set c % PF, then lands in
+  // LDS buffer c & 1; chunk c of the weights sits in ring slot c % PF.
+  u32x4_t areg[PF][PPT];
+  auto load_a = [&](int kc, u32x4_t (&dst)[PPT]) {
+#pragma unroll
+    for (int j = 0; j < PPT; j++) dst[j] = *(const u32x4_t*)(C.arow[j] + kc * KC);
+  };
+  // Thread tid stages pieces (tid + 256 j) mod PIECES: in small tiles some
+  // pieces are stored twice (same bytes, same place), so no store sits
+  // behind a branch.
+  auto store_a = [&](uint16_t* dst, const u32x4_t (&src)[PPT]) {
+#pragma unroll
+    for (int j = 0; j < PPT; j++) {
+      const int q = (tid + WAVES * 64 * j) % PIECES;
+      *(u32x4_t*)(dst + lds_a_index(q >> 3, q & 7)) = src[j];
+    }
+  };
+  const F16Consts f16k = {0x000f000fu, 0x00f000f0u, 0x64006400u};
+  // One chunk on all MAXMF row fragments.  Fragments past the tile's last row
+  // hold copies of its first row and are never stored: a straight-line run of
+  // MFMAs with no branch beats skipping them (a scalar branch per fragment
+  // breaks the MFMA issue stream).
+  auto compute = [&](const uint16_t* as, const WTile<FMT>& w) {
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const int ch = 4 * s + (lane >> 4);
+      u32x4_t av[NMF];
+#pragma unroll
+      for (int i = 0; i < NMF; i++)
+        av[i] = *(const u32x4_t*)(as + lds_a_index(i * 16 + (lane & 15), ch));
+#pragma unroll
+      for (int f = 0; f < 4; f++) {
+        const u32x4_t b = F16 ? w.template frag16<(MAXMF <= 2)>(f, s, f16k) : w.frag(f, s);
+#pragma unroll
+        for (int i = 0; i < NMF; i++)
+          acc[i][f] = F16 ? mfma16x16_f16(av[i], b, acc[i][f]) : mfma16x16(av[i], b, acc[i][f]);
+      }
+    }
+  };
+
+  // The loop is peeled so that no load sits behind a condition: step kc
+  // issues the activation and weight loads of chunk kc + PF, in the order
+  // they will be waited for.  The memory counter retires loads in issue
+  // order, so a wait then covers the chunk it needs and nothing issued after
+  // it, and PF chunks stay in flight.  nk is a multiple of PF (the ABI's width
+  // checks).
+  static_assert(PF == 2 || PF == 4, "load lead must be 2 or 4 chunks");
+  WTile<FMT> ring[PF];
+  const uint8_t* wnext = C.wt;
+#pragma unroll
+  for (int p = 0; p < PF; p++) {
+    load_a(p, areg[p]);
+    ring[p].template load<NT>(wnext, lane);
+    wnext += tb;
+  }
+  store_a(sm.a[0], areg[0]);
+  __syncthreads();
+  for (int kc0 = 0; kc0 < nk - PF; kc0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; p++) {
+      load_a(kc0 + p + PF, areg[p]);  // set p held chunk kc0 + p, already in LDS
+      compute(sm.a[p & 1], ring[p]);
+      ring[p].template load<NT>(wnext, lane);
+      wnext += tb;
+      store_a(sm.a[(p + 1) & 1], areg[(p + 1) % PF]);
+      __syncthreads();
+      // keep the scheduler from hoisting the next chunk's dequantization
+      // into this one (it would hold two chunks' registers at once)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; p++) {  // the last PF chunks: nothing more to load
+    compute(sm.a[p & 1], ring[p]);
+    if (p + 1 < PF) {
+      store_a(sm.a[(p + 1) & 1], areg[p + 1]);
+      __syncthreads();
+    }
+  }
+
+  const int quad = 4 * (lane >> 4);
+  store_wave_tile<FMT, STAGE, NMF, F16>(
+      A, J.shared, J.start, J.cnt, C.run, C.Fw, C.sect, acc,
+      [&](int i, int r) { return sm.wrow[i * 16 + quad + r]; },
+      [&](int i, int r) { return sm.xs[i * 16 + quad + r]; });
+}
+
+// F16: stage-1 tile on fp16 MFMA, A rows from the fp16 copy of the
+// activations (scaled per token by a power of two, undone in the epilogue).
+template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
+__device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm) {
+  constexpr int ROWS = MAXMF * 16;
+  constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
+  constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
+  static_assert(PPT <= 3, "A staging holds at most 3 pieces per thread");
+  const int tid = threadIdx.x, wave = tid >> 6;
+  TileCtx C;
+  C.Fw = J.shared ? A.Fs : A.F;
+  const int K = STAGE == 1 ? A.d : C.Fw;
+  C.nk = K / KC;
+  C.run = J.nb * WAVES + wave;
+  // the ABI requires ffn widths % 128 and d % 256: every wave of a block has
+  // a run of weight rows
+  static_assert(WAVES * H_COLS_WAVE == H_COLS_BLOCK && WAVES * OUT_COLS_WAVE == OUT_COLS_BLOCK,
+                "a block covers whole 64-row weight runs of every matrix");
+  const size_t tb = tile_bytes(FMT);
+  const uint8_t* blob = J.shared ? A.shared_blob
+                                 : A.routed_blob + (size_t)J.expert * expert_bytes(FMT, A.d, A.F);
+  C.sect = STAGE == 1 ? blob : blob + w1_bytes(FMT, A.d, C.Fw);
+  C.wt = C.sect + (size_t)C.run * C.nk * tb;
+
+  // rows of this tile: source row of the activations and folded router weight
+  for (int m = tid; m < ROWS; m += WAVES * 64) {
+    int src = -1;
+    float wf = 0.0f, xs = 1.0f;
+    if (m < J.cnt) {
+      if (STAGE == 1) {
+        if (J.shared) {
+          src = J.start + m;
+          wf = 1.0f;
+        } else {
+          const int f = A.perm[J.start + m];
+          src = f / A.k;
+          wf = A.topk_w[f];
+        }
+        if (F16) xs = A.xscale[src];
+      } else {
+        src = J.start + m;
+      }
+    }
+    sm.src[m] = src;
+    sm.wrow[m] = wf;
+    sm.xs[m] = xs;
+  }
+  __syncthreads();
+
+  const uint16_t* abase = STAGE == 1 ? (F16 ? (const uint16_t*)A.x16 : (const uint16_t*)A.hidden)
+                                     : (const uint16_t*)(J.shared ? A.h_shared : A.h_routed);
+  const size_t astride = STAGE == 1 ? (size_t)A.d : (size_t)C.Fw;
+  // Rows past the tile's end load the tile's first row: their accumulator
+  // rows are never stored, and every lane issues the same loads.
+#pragma unroll
+  for (int j = 0; j < PPT; j++) {
+    const int q = (tid + WAVES * 64 * j) % PIECES;  // piece q: row q / 8, 16-byte chunk q % 8
+    const int r = q >> 3;
+    const int s = sm.src[r] >= 0 ? sm.src[r] : sm.src[0];
+    C.arow[j] = abase + (size_t)s * astride + (q & 7) * 8;
+  }
+  tile_body<FMT, STAGE, MAXMF, PF_MAX, F16, NT>(A, J, sm, C);
+}
+
+// Grid: slot-major with the column block fastest *within an XCD*: block b runs
+// on XCD b % 8; slot = (b / (8*NB)) * 8 + b % 8, nb = (b / 8) % NB.  So all
+// column blocks of one row tile share an XCD (and its L2 copy of the gathered
+// activation rows), and empty slots spread evenly over the XCDs.
+__device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_routed,
+                                           int ncols_shared, int rows_per_tile, TileJob& J) {
+  const int b = blockIdx.x;
+  const int slot = (b / (8 * NB)) * 8 + (b & 7);
+  J.nb = (b >> 3) % NB;
+  if (slot < A.routed_slots) {
+    if (slot >= *A.ntiles) return false;
+    const int2 t = A.tiles[slot];
+    J.shared = false;
+    J.expert = t.x;
+    J.start = A.offsets[t.x] + t.y;
+    J.cnt = min(rows_per_tile, A.offsets[t.x + 1] - J.start);
+    return J.nb < ncols_routed;
+  }
+  const int s = slot - A.routed_slots;
+  if (s >= A.shared_slots) return false;
+  J.shared = true;
+  J.expert = -1;
+  J.start = s * rows_per_tile;
+  J.cnt = min(rows_per_tile, A.T - J.start);
+  return J.nb < ncols_shared;
+}
+
+// column blocks of a matrix with `runs` 64-row weight runs
+__host__ __device__ __forceinline__ int col_blocks(int runs) { return (runs + WAVES - 1) / WAVES; }
+
+template <int RF, int SF, int STAGE, int MAXMF, int PF>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
+  __shared__ __attribute__((aligned(16))) Smem<MAXMF> sm;
+  const int nr = STAGE == 1 ? col_blocks(A.F / H_COLS_WAVE) : col_blocks(A.d / OUT_COLS_WAVE);
+  const int ns = STAGE == 1 ? (A.n_shared ? col_blocks(A.Fs / H_COLS_WAVE) : 0) : nr;
+  TileJob J;
+  if (!decode_job(A, max(nr, ns), nr, ns, MAXMF * 16, J)) return;
+  // int4 routed layers run gate/up on fp16 MFMA (the fp16 activation copy
+  // exists); int8 shared tiles of such a layer follow; bf16 weights stay bf16
+  constexpr bool X16 = x16_path(RF, MAXMF);
+  // Routed weights of a small-T call are read exactly once: stream them.  The
+  // shared expert's weights are re-read by every row tile, and a prefill
+  // expert can span two tiles: keep those cacheable.
+  constexpr bool NT_ROUTED = MAXMF <= 2, NT_SHARED = false;
+  if (J.shared)
+    run_tile<SF, STAGE, MAXMF, PF, STAGE == 1 && X16 && SF == MOE_I8_ROW, NT_SHARED>(A, J, sm);
+  else
+    run_tile<RF, STAGE, MAXMF, PF, STAGE == 1 && X16, NT_ROUTED>(A, J, sm);
+}
+
+// Row tiles come from the route plan (at most BM = 96 rows each).  A call
+// with at most 16 or 32 tokens has at most that many rows per expert (a token
+// picks an expert once), so it runs a kernel built for 1 or 2 row fragments
+// with a deeper weight prefetch; shared-expert tiles then hold 16 or 32 tokens.
+template <int RF, int SF, int MAXMF, int PF>
+static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
+  FfnArgs a = a0;
+  a.shared_slots = a.n_shared ? (a.T + MAXMF * 16 - 1) / (MAXMF * 16) : 0;
+  const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
+  const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
+  const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
+  if (x16_path(RF, MAXMF)) {
+    hipError_t e = launch_x_to_f16(a, s);
+    if (e != hipSuccess) return e;
+  }
+  ffn_kernel<RF, SF, 1, MAXMF, PF><<<slots * nb1, WAVES * 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ffn_kernel<RF, SF, 2, MAXMF, PF><<<slots * nb2, WAVES * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int RF, int SF>
+static hipError_t launch_pair(const FfnArgs& a, hipStream_t s) {
+  if (a.T <= 16) return launch_stages<RF, SF, 1, LEAD_I4>(a, s);
+  if (a.T <= 32) return launch_stages<RF, SF, 2, LEAD_I4>(a, s);
+  return launch_stages<RF, SF, BM / 16, LEAD_I4>(a, s);
+}
+
+}  // namespace moe

@@ -43,8 +43,26 @@ constexpr int PLAN_THREADS = 1024; // 16 waves
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 32;
 
+// Bits per code of the group-32 integer formats (4 for MOE_I4_G32), else 0.
+__host__ __device__ constexpr int ig32_bits(int fmt) {
+  return fmt == MOE_I4_G32 ? 4 : fmt == MOE_I2_G32 ? 2 : fmt == MOE_I3_G32 ? 3
+       : fmt == MOE_I5_G32 ? 5 : fmt == MOE_I6_G32 ? 6 : fmt == MOE_I7_G32 ? 7
+       : fmt == MOE_I8_G32 ? 8 : 0;
+}
+// b-bit group-32 wave tile: 64 lanes x 8b bytes of codes, then the 256 bytes
+// of fp16 group scales (b = 4 gives the int4 tile's 2304 bytes)
+__host__ __device__ constexpr int tile_bytes_ig32(int b) { return 512 * b + 256; }
+
 __host__ __device__ inline size_t tile_bytes(int fmt) {
-  return fmt == MOE_BF16 ? TILE_BYTES_BF16 : fmt == MOE_I4_G32 ? TILE_BYTES_I4 : TILE_BYTES_I8;
+  return fmt == MOE_BF16 ? TILE_BYTES_BF16
+       : fmt == MOE_I4_G32 ? TILE_BYTES_I4
+       : fmt == MOE_I8_ROW ? TILE_BYTES_I8
+       : tile_bytes_ig32(ig32_bits(fmt));
+}
+// K chunks each wave keeps in flight for a weight format: 4- and 2-bit codes
+// take LEAD_I4, the other tiles LEAD_WIDE (their registers)
+__host__ __device__ constexpr int lead_of(int fmt, int lead_i4) {
+  return (ig32_bits(fmt) == 4 || ig32_bits(fmt) == 2) ? lead_i4 : LEAD_WIDE;
 }
 
 // Bytes of the W1 (gate/up, [2F, d]) and W2 (down, [d, F]) sections of one
@@ -93,7 +111,7 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 8);
   L.h_routed = off; off = align256(off + (size_t)n * D.ffn * elem);
   L.h_shared = off; off = align256(off + (D.n_shared ? (size_t)T * D.shared_ffn * elem : 0));
-  const bool x16 = D.act == MOE_BF16 && D.expert_w == MOE_I4_G32;
+  const bool x16 = D.act == MOE_BF16 && ig32_bits(D.expert_w) != 0;
   L.x16 = off;      off = align256(off + (x16 ? (size_t)T * D.d * 2 : 0));
   L.xexp = off;     off = align256(off + (x16 ? (size_t)T * 4 : 0));
   L.total = off;
@@ -131,6 +149,8 @@ struct FfnArgs {
 };
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+// routed weights in the 2, 3, 5, 6, 7 or 8-bit group-32 formats
+hipError_t launch_ffn_lowbit(const FfnArgs& a, hipStream_t s);
 // x -> fp16 copy and per-token scale (int4 layers)
 hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,

@@ -163,11 +163,96 @@ struct WTile<MOE_I8_ROW> {
   }
 };
 
-// Gate/up of int4 layers runs fp16 MFMA on the fp16 copy of x: its int4 ->
-// fp16 conversion costs fewer VALU ops than bf16, which sets the speed of the
-// large-T loop and still shows in the weight-streaming small-T one.
+// ---- b-bit group-32 codes (b = 2, 3, 5, 6, 7, 8) ------------------------
+// Lane l's codes of a wave tile form one little-endian bit stream of 64 b
+// bits: code i (0..7) of fragment f, K step s at bit (2 f + s) 8 b + i b, as
+// code + 2^(b-1) (offset binary).  The stream's dwords sit in 16-byte groups
+// (group g of all lanes at g*1024 + lane*16), an odd b ending with one
+// 8-byte group (at G*1024 + lane*8); the fp16 group scales follow at 512 b,
+// as in the int4 tile.  So every load is a coalesced wave-wide run and the
+// blob holds exactly b bits per weight plus the scales.
+template <int B>
+struct WTileB {
+  static constexpr int NDW = 2 * B;    // stream dwords per lane
+  static constexpr int G = NDW / 4;    // full 16-byte groups
+  static constexpr bool TAIL = NDW % 4 != 0;
+  uint32_t w[NDW];
+  u32x4_t sc;
+  template <bool NT>
+  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      const u32x4_t v = ldw<NT>(t + g * 1024, lane);
+#pragma unroll
+      for (int c = 0; c < 4; c++) w[4 * g + c] = v[c];
+    }
+    if constexpr (TAIL) {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t* p = (const u32x2_t*)(t + G * 1024) + lane;
+      const u32x2_t v = NT ? __builtin_nontemporal_load(p) : *p;
+      w[4 * G] = v[0];
+      w[4 * G + 1] = v[1];
+    }
+    sc = ldw<NT>(t + 512 * B, lane & 15);
+  }
+  __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
+    const int si = f * 2 + s;
+    const uint32_t sw = sc[si >> 1];
+    return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
+  }
+  // bits [o, o + n) of the stream, n <= 16 (o, n constant once unrolled)
+  __device__ __forceinline__ uint32_t field(int o, int n) const {
+    const int d = o >> 5, sh = o & 31;
+    const uint32_t win = sh + n <= 32 ? w[d] >> sh : __builtin_amdgcn_alignbit(w[d + 1], w[d], sh);
+    return win & ((1u << n) - 1);
+  }
+  // fp16(code * scale): each pair of codes under the fp16 exponent of 1024
+  // reads as 1024 + code + 2^(b-1); one packed subtract makes the codes exact,
+  // one packed multiply by the scale rounds each product to nearest even.
+  template <bool>
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
+    const uint32_t sb = scale_bits(f, s);
+    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
+    constexpr _Float16 bias = (_Float16)(-(1024 + (1 << (B - 1))));
+    const f16x2_t off = {bias, bias};
+    const int base = (2 * f + s) * 8 * B;
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t lo = field(base + 2 * j * B, B), hi = field(base + (2 * j + 1) * B, B);
+      const uint32_t t = ((hi << 16) | lo) | 0x64006400u;
+      r[j] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, t) + off) * s2);
+    }
+    return r;
+  }
+  // bf16(code * scale): code + 2^(b-1) as a float, one FMA with the scale
+  // (exact in fp32), rounded to nearest even by the pack
+  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+    const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
+    const float bias = -(float)(1 << (B - 1)) * scale;
+    const int base = (2 * f + s) * 8 * B;
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float a = (float)field(base + 2 * j * B, B), b = (float)field(base + (2 * j + 1) * B, B);
+      r[j] = pack_bf16x2(fmaf(a, scale, bias), fmaf(b, scale, bias));
+    }
+    return r;
+  }
+};
+template <> struct WTile<MOE_I2_G32> : WTileB<2> {};
+template <> struct WTile<MOE_I3_G32> : WTileB<3> {};
+template <> struct WTile<MOE_I5_G32> : WTileB<5> {};
+template <> struct WTile<MOE_I6_G32> : WTileB<6> {};
+template <> struct WTile<MOE_I7_G32> : WTileB<7> {};
+template <> struct WTile<MOE_I8_G32> : WTileB<8> {};
+
+// Gate/up of int4 (and b-bit group-32) layers runs fp16 MFMA on the fp16
+// copy of x: their code -> fp16 conversion costs fewer VALU ops than bf16,
+// which sets the speed of the large-T loop and still shows in the
+// weight-streaming small-T one.
 __host__ __device__ constexpr bool x16_path(int routed_fmt, int) {
-  return routed_fmt == MOE_I4_G32;
+  return ig32_bits(routed_fmt) != 0;
 }
 
 __device__ __forceinline__ float silu_fast(float g) {

@@ -14,6 +14,10 @@
  *     uses a deterministic stable top-k (moe_route).
  *   - same README, "Model artifact and memory placement" table: routed experts
  *     stored as symmetric grouped int4/int8, the router kept unquantized.
+ *   - TandemLLM roadmap, "A mixture-of-experts model, and what is left", and
+ *     chapter 17, section 17.2: expert packs coded at other bit widths, MoE
+ *     kernels that take 2 to 6 and 8 bits (here 2, 3, 5, 6, 7 and 8-bit
+ *     group-32 codes beside int4).
  *
  * Conventions for every call below:
  *   - Ownership: the caller allocates and frees every buffer.  The library
@@ -42,6 +46,11 @@
  *     fp16 scale per 32 consecutive elements along K, scales [rows, K/32].
  *     Weight value = code * scale.
  *   MOE_I8_ROW: int8 codes in [-127, 127], one fp16 scale per row, scales [rows].
+ *   MOE_I2_G32 .. MOE_I8_G32 (b = 2, 3, 5, 6, 7, 8 bits): symmetric b-bit codes
+ *     in [-(2^(b-1) - 1), 2^(b-1) - 1], one int8 per code, [rows, K]; one fp16
+ *     scale per 32 consecutive elements along K, scales [rows, K/32].  Weight
+ *     value = code * scale.  The device blob stores them at b bits per weight
+ *     (plus the scales).
  * The device blob written by moe_pack_experts is a private, tile-ordered
  * layout; its only contract is moe_pack_experts / moe_unpack_experts.
  */
@@ -69,7 +78,13 @@ typedef enum moe_dtype {
   MOE_F32 = 0,    /* IEEE binary32                                     */
   MOE_BF16 = 1,   /* bfloat16                                          */
   MOE_I4_G32 = 2, /* symmetric int4 + fp16 scale per 32 along K        */
-  MOE_I8_ROW = 3  /* symmetric int8 + fp16 scale per output row        */
+  MOE_I8_ROW = 3, /* symmetric int8 + fp16 scale per output row        */
+  MOE_I2_G32 = 4, /* symmetric b-bit codes + fp16 scale per 32 along K  */
+  MOE_I3_G32 = 5,
+  MOE_I5_G32 = 6,
+  MOE_I6_G32 = 7,
+  MOE_I7_G32 = 8,
+  MOE_I8_G32 = 9
 } moe_dtype;
 
 typedef enum moe_blob_kind {
@@ -80,10 +95,10 @@ typedef enum moe_blob_kind {
 /* Shape and storage of one MoE layer.
  * Supported combinations:
  *   act MOE_F32 : expert_w MOE_F32, shared_w MOE_F32 (router fp32, y fp32)
- *   act MOE_BF16: expert_w MOE_BF16 or MOE_I4_G32,
+ *   act MOE_BF16: expert_w MOE_BF16, MOE_I4_G32 or MOE_I{2,3,5,6,7,8}_G32,
  *                 shared_w MOE_BF16 or MOE_I8_ROW  (router bf16, y bf16)
  * Sizes: 1 <= n_experts <= 1024; n_shared 0 or 1.  For act MOE_BF16:
- * d % 256 == 0, ffn % 128 == 0 (% 256 with I4_G32 routed weights),
+ * d % 256 == 0, ffn % 128 == 0 (% 256 with 2- or 4-bit routed weights),
  * shared_ffn % 128 == 0.  For act MOE_F32:
  * d, ffn, shared_ffn multiples of 64.  d, ffn, shared_ffn <= 16384.         */
 typedef struct moe_desc {
@@ -118,7 +133,8 @@ moe_status moe_blob_bytes(const moe_desc* desc, int32_t kind, size_t* bytes);
  * (>= moe_blob_bytes).  The caller copies it to device memory.  For ROUTED the
  * inputs hold n_experts experts stacked; for SHARED one expert.
  * MOE_I4_G32 codes must lie in [-7, 7] (symmetric); an 8 (-8) code returns
- * MOE_EINVAL.  Host only.                                                   */
+ * MOE_EINVAL, as does a b-bit code outside [-(2^(b-1) - 1), 2^(b-1) - 1].
+ * Host only.                                                                */
 moe_status moe_pack_experts(const moe_desc* desc, int32_t kind, const void* gate,
                             const void* gate_scales, const void* up, const void* up_scales,
                             const void* down, const void* down_scales, void* blob,
@@ -186,11 +202,12 @@ moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const int32_t
  *   workspace   the workspace moe_permute filled (holds its tile plan and the
  *               intermediate h).
  * Arithmetic (act BF16): MFMA with fp32 accumulation.  bf16 weights run bf16
- * MFMA.  With int4 routed weights the gate/up products run fp16 MFMA on an
- * fp16 copy of x, each token row scaled by a power of two so its largest
- * magnitude lies in [2^14, 2^15) (undone on the fp32 accumulator); int4
- * weights become fp16(code * scale) there and bf16(code * scale) in the
- * down product; int8 codes enter exactly, their row scale applied to the
+ * MFMA.  With int4 (or other b-bit group-32) routed weights the gate/up
+ * products run fp16 MFMA on an fp16 copy of x, each token row scaled by a
+ * power of two so its largest magnitude lies in [2^14, 2^15) (undone on the
+ * fp32 accumulator); the codes become fp16(code * scale) there and
+ * bf16(code * scale) in the down product; int8 codes enter exactly, their row
+ * scale applied to the
  * fp32 accumulator.  h is rounded to bf16 (nearest even); the outputs stay
  * fp32.  The fp32 path computes and stores in fp32 throughout.              */
 moe_status moe_grouped_ffn(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,

@@ -27,7 +27,10 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.environ.get("ORC_LIB_OVERRIDE") or os.path.join(_HERE, "liborc.so")
 
 F32, BF16, I4G32, I8ROW = 0, 1, 2, 3
-FMT_NAMES = {"f32": F32, "bf16": BF16, "i4g32": I4G32, "i8row": I8ROW}
+IG32 = 16  # + b: b-bit symmetric codes, one int8 each, fp16 scale per 32 along K
+I2G32, I3G32, I5G32, I6G32, I7G32, I8G32 = (IG32 + b for b in (2, 3, 5, 6, 7, 8))
+FMT_NAMES = {"f32": F32, "bf16": BF16, "i4g32": I4G32, "i8row": I8ROW, "i2g32": I2G32,
+             "i3g32": I3G32, "i5g32": I5G32, "i6g32": I6G32, "i7g32": I7G32, "i8g32": I8G32}
 
 _lib = None
 

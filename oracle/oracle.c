@@ -28,7 +28,12 @@
  *   - route plan: stable counting sort of flat index f = t*k + s by expert;
  *   - int4: two's complement nibbles, element 2j in the low nibble, value
  *     q * s with one fp16 scale per 32 consecutive elements along K;
- *     int8: value q * s with one fp16 scale per output row.
+ *     int8: value q * s with one fp16 scale per output row;
+ *     b-bit codes (b = 2, 3, 5, 6, 7, 8; TandemLLM roadmap, "A mixture-of-
+ *     experts model, and what is left", and chapter 17, section 17.2: expert
+ *     packs at other bit widths): one int8 per code, symmetric range
+ *     [-(2^(b-1) - 1), 2^(b-1) - 1], value q * s with one fp16 scale per 32
+ *     consecutive elements along K.
  *
  * Every arithmetic step runs in double precision on the exact upcast of the
  * stored values.  There is no blocking, fusion or reordering: each function
@@ -43,6 +48,11 @@
 #define ORC_BF16 1  /* bfloat16 bit patterns (uint16)                   */
 #define ORC_I4G32 2 /* int4 two's complement + fp16 scale per 32 along K */
 #define ORC_I8ROW 3 /* int8 + fp16 scale per row                        */
+#define ORC_IG32 16 /* + b: b-bit codes (one int8 each) + fp16 scale per 32 along K */
+static int ig32_bits(int fmt) {
+  const int b = fmt - ORC_IG32;
+  return (b >= 2 && b <= 8 && b != 4) ? b : 0;
+}
 
 #define ORC_OK 0
 #define ORC_EINVAL -1
@@ -85,7 +95,9 @@ static int nibble_value(const uint8_t* row, int64_t j) {
  *   F32 : q = float[rows*K]
  *   BF16: q = uint16[rows*K]
  *   I4G32: q = uint8[rows*K/2], scales = uint16 (fp16) [rows*K/32]
- *   I8ROW: q = int8[rows*K],    scales = uint16 (fp16) [rows]           */
+ *   I8ROW: q = int8[rows*K],    scales = uint16 (fp16) [rows]
+ *   IG32+b: q = int8[rows*K],   scales = uint16 (fp16) [rows*K/32]; a code
+ *           outside [-(2^(b-1) - 1), 2^(b-1) - 1] is an error              */
 int orc_decode_matrix(int fmt, int64_t rows, int64_t K, const void* q, const void* scales,
                       double* out) {
   if (rows < 0 || K < 0 || (rows * K > 0 && (!q || !out))) return ORC_EINVAL;
@@ -105,6 +117,13 @@ int orc_decode_matrix(int fmt, int64_t rows, int64_t K, const void* q, const voi
         if (!scales) return ORC_EINVAL;
         double s = orc_f16_to_f64(((const uint16_t*)scales)[r]);
         v = (double)((const int8_t*)q)[r * K + j] * s;
+      } else if (ig32_bits(fmt)) {
+        if (K % 32 != 0 || !scales) return ORC_EINVAL;
+        const int lim = (1 << (ig32_bits(fmt) - 1)) - 1;
+        const int c = ((const int8_t*)q)[r * K + j];
+        if (c < -lim || c > lim) return ORC_EINVAL;
+        double s = orc_f16_to_f64(((const uint16_t*)scales)[r * (K / 32) + j / 32]);
+        v = (double)c * s;
       } else {
         return ORC_EINVAL;
       }
@@ -122,10 +141,11 @@ static int64_t q_bytes(int fmt, int64_t rows, int64_t K) {
     case ORC_I4G32: return rows * K / 2;
     case ORC_I8ROW: return rows * K;
   }
+  if (ig32_bits(fmt)) return rows * K;
   return -1;
 }
 static int64_t s_bytes(int fmt, int64_t rows, int64_t K) {
-  if (fmt == ORC_I4G32) return rows * (K / 32) * 2;
+  if (fmt == ORC_I4G32 || ig32_bits(fmt)) return rows * (K / 32) * 2;
   if (fmt == ORC_I8ROW) return rows * 2;
   return 0;
 }

@@ -9,7 +9,8 @@ import oracle
 import workloads as W
 from expert_grouped_quantized_amd.layer import MoELayer, blobs_from_inputs
 
-ORC_FMT = {W.F32: oracle.F32, W.BF16: oracle.BF16, W.I4G32: oracle.I4G32, W.I8ROW: oracle.I8ROW}
+ORC_FMT = {W.F32: oracle.F32, W.BF16: oracle.BF16, W.I4G32: oracle.I4G32, W.I8ROW: oracle.I8ROW,
+           **{name: oracle.FMT_NAMES[name] for name in W.IG32.values()}}
 
 
 def desc_of(cfg: W.LayerConfig):

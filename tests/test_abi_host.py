@@ -53,7 +53,7 @@ def _route(desc, T=4, k=10, hidden=FAKE, rw=FAKE, bias=None, logits=FAKE, ids=FA
     (dict(n_shared=2), M.MOE_EINVAL, "n_shared"),
     (dict(d=2500), M.MOE_EUNSUPPORTED, "d % 256"),
     (dict(ffn=1000), M.MOE_EUNSUPPORTED, "ffn"),
-    (dict(ffn=1152), M.MOE_EUNSUPPORTED, "I4_G32 routed experts need ffn % 256"),
+    (dict(ffn=1152), M.MOE_EUNSUPPORTED, "4-bit routed experts need ffn % 256"),
     (dict(act="i4g32"), M.MOE_EUNSUPPORTED, "act"),
     (dict(expert_w="i8row"), M.MOE_EUNSUPPORTED, "routed"),
     (dict(shared_w="i4g32"), M.MOE_EUNSUPPORTED, "shared"),
@@ -147,7 +147,8 @@ def _rand_expert(fmt, rows, K, n, rng):
 
 @pytest.mark.parametrize("act,fmt,kind", [("bf16", "bf16", 0), ("bf16", "i4g32", 0),
                                           ("bf16", "i8row", 1), ("bf16", "bf16", 1),
-                                          ("f32", "f32", 0), ("f32", "f32", 1)])
+                                          ("f32", "f32", 0), ("f32", "f32", 1)]
+                         + [("bf16", f, 0) for f in W.IG32.values()])
 def test_pack_unpack_roundtrip(act, fmt, kind):
     rng = np.random.default_rng(hash((act, fmt, kind)) % 2**32)
     d, F, E = (256, 256, 3) if act == "bf16" else (128, 64, 2)
@@ -182,4 +183,40 @@ def test_pack_rejects_int4_minus_eight():
     blob = np.empty(M.moe_blob_bytes(desc, 0), np.uint8)
     with pytest.raises(M.MoeError) as ei:
         M.moe_pack_experts(desc, 0, g, s, g, s, dq, dsc, blob)
-    assert ei.value.status == M.MOE_EINVAL and "-8" in str(ei.value)
+    assert ei.value.status == M.MOE_EINVAL and "outside [-7, 7]" in str(ei.value)
+
+
+@pytest.mark.parametrize("b", sorted(W.IG32))
+def test_pack_rejects_codes_outside_the_symmetric_range(b):
+    lim = (1 << (b - 1)) - 1
+    desc = M.make_desc(256, 1, 256, 0, 0, act="bf16", expert_w=W.IG32[b])
+    s = np.full((1, 256, 8), 0x3C00, np.uint16)
+    z = np.zeros((1, 256, 256), np.int8)
+    blob = np.empty(M.moe_blob_bytes(desc, 0), np.uint8)
+    M.moe_pack_experts(desc, 0, z + lim, s, z - lim, s, z, s, blob)  # the extremes are fine
+    for bad in (lim + 1, -lim - 1):
+        if not -128 <= bad <= 127:  # 8-bit: only -128 lies outside and fits a byte
+            continue
+        q = z.copy()
+        q[0, 3, 200] = bad
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_pack_experts(desc, 0, z, s, z, s, q, s, blob)
+        assert ei.value.status == M.MOE_EINVAL and f"[{-lim}, {lim}]" in str(ei.value)
+
+
+@pytest.mark.parametrize("b", sorted(W.IG32))
+def test_blob_bytes_of_bbit_codes(b):
+    desc = _desc(expert_w=W.IG32[b])
+    per_w = 3 * 1024 * 2560
+    # b bits per weight plus one fp16 scale per 32 weights, nothing else
+    assert M.moe_blob_bytes(desc, M.MOE_BLOB_ROUTED) == 512 * per_w * (2 * b + 1) // 16
+
+
+def test_bbit_formats_only_for_routed_weights_and_2bit_needs_ffn_256():
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_blob_bytes(_desc(shared_w="i5g32"), 0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_blob_bytes(M.make_desc(256, 4, 384, 0, 0, act="bf16", expert_w="i2g32"), 0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED and "256" in str(ei.value)
+    M.moe_blob_bytes(M.make_desc(256, 4, 384, 0, 0, act="bf16", expert_w="i3g32"), 0)

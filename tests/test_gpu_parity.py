@@ -70,6 +70,13 @@ def _small_cfg(name, idx, **kw):
     _small_cfg("wide_E1024", 7, E=1024, k=8, T=96, n_shared=0, Fs=0),
     _small_cfg("f32_ragged", 8, act=W.F32, router=W.F32, expert=W.F32, shared=W.F32, T=99,
                d=128, F=64, Fs=128),
+    # b-bit group-32 routed experts (2, 3, 5, 6, 7, 8 bits), every tile size
+    _small_cfg("i2_T300", 20, expert=W.IG32[2]),
+    _small_cfg("i3_T300_d512", 21, expert=W.IG32[3], d=512, F=384),
+    _small_cfg("i5_bf16shared", 22, expert=W.IG32[5], shared=W.BF16, T=129),
+    _small_cfg("i6_T20", 23, expert=W.IG32[6], T=20),
+    _small_cfg("i7_T5", 24, expert=W.IG32[7], T=5),
+    _small_cfg("i8g_T77", 25, expert=W.IG32[8], T=77, F=128),
 ], ids=lambda c: c.name)
 def test_small_shapes_full(cfg):
     inp = W.generate(cfg)
@@ -178,7 +185,8 @@ def test_graph_replay_matches_eager(T):
         assert np.array_equal(L.y[:T].view(torch.int16).cpu().numpy(), y_b), f"replay {i} (b)"
 
 
-@pytest.mark.parametrize("expert,shared", [(W.I4G32, W.I8ROW), (W.BF16, W.BF16)])
+@pytest.mark.parametrize("expert,shared", [(W.I4G32, W.I8ROW), (W.BF16, W.BF16),
+                                           (W.IG32[5], W.I8ROW)])
 def test_rows_do_not_depend_on_the_batch(expert, shared):
     """A token's logits and output bits are the same whichever kernels its
     call size selects: 300 tokens (large-T router, 96-row tiles), 40 (small-T

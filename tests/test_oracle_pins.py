@@ -72,7 +72,48 @@ def test_int8_row_decoder_all_codes(orc):
     assert np.array_equal(got, q.astype(np.float64) * np.array([[0.5], [-3.0]]))
 
 
-@pytest.mark.parametrize("fmt,bound_div", [(W.I4G32, 2.0), (W.I8ROW, 2.0)])
+@pytest.mark.parametrize("b", sorted(W.IG32))
+def test_bbit_decoder_every_code_and_group_scale_index(orc, b):
+    """b-bit group-32 codes: every code of the symmetric range decodes to
+    code * scale(row, j // 32), with a distinct power-of-two scale per
+    (row, group) so a shifted or transposed scale index shows."""
+    lim = (1 << (b - 1)) - 1
+    codes = np.arange(-lim, lim + 1)
+    rows, K = 3, 32 * ((len(codes) + 31) // 32 + 1)
+    q = np.resize(codes, rows * K).reshape(rows, K).astype(np.int8)
+    g = np.arange(K // 32)[None, :]
+    exps = (g + 5 * np.arange(rows)[:, None]) % 15     # normal fp16 powers of two
+    scales = np.array(2.0 ** -exps, np.float16).view(np.uint16)
+    got = orc.decode_matrix(orc.FMT_NAMES[W.IG32[b]], rows, K, q, scales)
+    assert np.array_equal(got, q.astype(np.float64) * np.repeat(2.0 ** -exps, 32, axis=1))
+
+
+@pytest.mark.parametrize("b", sorted(W.IG32))
+def test_bbit_decoder_rejects_codes_outside_the_range(orc, b):
+    lim = (1 << (b - 1)) - 1
+    s = np.full(1, 0x3C00, np.uint16)
+    for bad in (lim + 1, -lim - 1):
+        if not -128 <= bad <= 127:
+            continue
+        q = np.zeros(32, np.int8)
+        q[9] = bad
+        with pytest.raises(RuntimeError):
+            orc.decode_matrix(orc.FMT_NAMES[W.IG32[b]], 1, 32, q, s)
+
+
+def test_8bit_groups_with_one_scale_per_row_equal_int8_rows(orc):
+    """8-bit group-32 codes whose groups share one scale per row decode exactly
+    like the int8 per-row format (a different decoder of the same values)."""
+    rng = np.random.default_rng(3)
+    q = rng.integers(-127, 128, size=(5, 96)).astype(np.int8)
+    row_s = np.array(rng.uniform(0.01, 2.0, 5), np.float16)
+    g = orc.decode_matrix(orc.I8G32, 5, 96, q, np.repeat(row_s.view(np.uint16)[:, None], 3, axis=1))
+    r = orc.decode_matrix(orc.I8ROW, 5, 96, q, row_s.view(np.uint16))
+    assert np.array_equal(g, r)
+
+
+@pytest.mark.parametrize("fmt,bound_div", [(W.I4G32, 2.0), (W.I8ROW, 2.0)]
+                         + [(f, 2.0) for f in W.IG32.values()])
 def test_quantize_roundtrip_bound(orc, fmt, bound_div):
     """Symmetric round-to-nearest: |decode(quantize(w)) - w| <= s/2 (+ fp16 slack)."""
     rng = np.random.default_rng(7)
@@ -80,7 +121,7 @@ def test_quantize_roundtrip_bound(orc, fmt, bound_div):
     q, s = W.store(w, fmt)
     dec = orc.decode_matrix(orc.FMT_NAMES[fmt], 64, 256, q, s)
     sv = s.view(np.float16).astype(np.float64)
-    per = np.repeat(sv, 32, axis=1) if fmt == W.I4G32 else sv[:, None]
+    per = sv[:, None] if fmt == W.I8ROW else np.repeat(sv, 32, axis=1)
     # the scale is fp16-rounded, so max|w|/s may exceed the top code by < 1 ulp
     assert np.all(np.abs(dec - w) <= per / bound_div * (1 + 2e-3) + 1e-12)
 
@@ -374,6 +415,33 @@ def test_quantized_layer_equals_decoded_f32_layer(orc):
     for k in ("wg", "wu", "wd", "sg", "su", "sd"):                 # exact in fp32
         assert np.array_equal(inp_f[k].astype(np.float64),
                               (dec4 if k[0] == "w" else dec8)(inp[k], inp[k + "_s"]))
+    y_q, _, _ = _layer(orc, inp, wr, spec_q)
+    y_f, _, _ = _layer(orc, inp_f, wr, _spec(64, 6, 2, 32, 1, 32))
+    np.testing.assert_allclose(y_q, y_f, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("b", [2, 3, 6])
+def test_bbit_layer_equals_decoded_f32_layer(orc, b):
+    """b-bit group-32 routed experts: the layer equals the same layer on the
+    decoded values (numpy: code * fp16 group scale, exact in fp32)."""
+    fmt = W.IG32[b]
+    inp, wr = _tiny_inputs(fmt=fmt, sfmt=W.I8ROW)
+    spec_q = _spec(64, 6, 2, 32, 1, 32, 0, orc.FMT_NAMES[fmt], orc.I8ROW)
+
+    def decb(q, s):
+        return q.astype(np.float64) * np.repeat(s.view(np.float16).astype(np.float64), 32, axis=-1)
+
+    def dec8(q, s):
+        return q.astype(np.float64) * s.view(np.float16).astype(np.float64)[:, None]
+
+    inp_f = dict(x=inp["x"], wg=decb(inp["wg"], inp["wg_s"]).astype(np.float32),
+                 wu=decb(inp["wu"], inp["wu_s"]).astype(np.float32),
+                 wd=decb(inp["wd"], inp["wd_s"]).astype(np.float32),
+                 sg=dec8(inp["sg"], inp["sg_s"]).astype(np.float32),
+                 su=dec8(inp["su"], inp["su_s"]).astype(np.float32),
+                 sd=dec8(inp["sd"], inp["sd_s"]).astype(np.float32))
+    lim = (1 << (b - 1)) - 1
+    assert max(np.abs(inp[k]).max() for k in ("wg", "wu", "wd")) <= lim
     y_q, _, _ = _layer(orc, inp, wr, spec_q)
     y_f, _, _ = _layer(orc, inp_f, wr, _spec(64, 6, 2, 32, 1, 32))
     np.testing.assert_allclose(y_q, y_f, rtol=0, atol=1e-13)

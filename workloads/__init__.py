@@ -20,6 +20,8 @@ Recipe (every draw seeded; PCG64 streams keyed by (seed, role[, expert])):
   bf16 storage      round-to-nearest-even of the fp32 draw
   int4 g32          s = fp16(max|w_group|/7), q = clip(rint(w/s), -7, 7); s=0 -> q=0
   int8 per row      s = fp16(max|w_row|/127), q = clip(rint(w/s), -127, 127)
+  b-bit g32         s = fp16(max|w_group|/(2^(b-1)-1)), q = clip(rint(w/s), +-(2^(b-1)-1)),
+                    b = 2, 3, 5, 6, 7, 8 (one int8 per code)
   Zipf bias         bias_e = -c * 1.1 * ln(r_e), r a seeded permutation of 1..E,
                     c = ZIPF_C (chosen so the hottest expert gets about 10x the
                     mean load on the seeded T=16384 input).
@@ -33,6 +35,9 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 F32, BF16, I4G32, I8ROW = "f32", "bf16", "i4g32", "i8row"
+# b-bit group-32 formats: symmetric codes, one int8 each, fp16 scale per 32 along K
+IG32 = {2: "i2g32", 3: "i3g32", 5: "i5g32", 6: "i6g32", 7: "i7g32", 8: "i8g32"}
+IG32_BITS = {v: b for b, v in IG32.items()}
 ZIPF_S = 1.1
 ZIPF_C = 0.22
 
@@ -113,6 +118,21 @@ def pack_int4(q: np.ndarray) -> np.ndarray:
     return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
 
 
+def quantize_ig32(w: np.ndarray, b: int):
+    """[rows, K] float -> (int8 codes [rows, K] in [-(2^(b-1)-1), 2^(b-1)-1],
+    fp16 bits [rows, K/32]); s = fp16(max|w_group| / (2^(b-1)-1))."""
+    rows, K = w.shape
+    assert K % 32 == 0
+    qmax = (1 << (b - 1)) - 1
+    g = w.reshape(rows, K // 32, 32).astype(np.float32)
+    s16 = (np.abs(g).max(axis=2) / np.float32(qmax)).astype(np.float16)
+    s = s16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(g / np.where(s > 0, s, 1)), 0)
+    q = np.clip(q, -qmax, qmax).astype(np.int8).reshape(rows, K)
+    return q, s16.view(np.uint16)
+
+
 def quantize_i8row(w: np.ndarray):
     """[rows, K] float -> (int8 [rows, K], fp16 bits [rows])."""
     w = w.astype(np.float32)
@@ -133,6 +153,8 @@ def store(w: np.ndarray, fmt: str):
         return quantize_i4g32(w)
     if fmt == I8ROW:
         return quantize_i8row(w)
+    if fmt in IG32_BITS:
+        return quantize_ig32(w, IG32_BITS[fmt])
     raise ValueError(fmt)
 
 
