@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
-    p.add_argument("--workload", choices=("both", "prefill", "decode"), default="both",
+    p.add_argument("--workload", choices=("both", "prefill", "decode", "bits"), default="both",
                    help="limit the run to one workload (for per-workload profiles)")
     return p.parse_args()
 
@@ -172,7 +172,9 @@ def measured_peaks(torch):
 def algorithmic(cfg, T, n_active):
     """Flops and bytes of one layer call (the definition, not what the kernels move)."""
     d, F, Fs, k, E = cfg.d, cfg.F, cfg.Fs, cfg.k, cfg.E
+    import workloads as W
     wbytes = {"i4g32": 0.5 + 2 / 32, "bf16": 2.0, "i8row": 1.0}
+    wbytes.update({name: b / 8 + 2 / 32 for b, name in W.IG32.items()})
     ffn_flops = 6.0 * T * k * d * F + 6.0 * T * d * Fs
     router_flops = 2.0 * T * E * d
     per_expert = 3 * d * F * wbytes[cfg.expert]
@@ -218,7 +220,7 @@ def counted_traffic(workload: str):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
-    for f in ("ffn.hip", "wave_tile.h", "moe_internal.h", "device_common.h"):
+    for f in ("ffn.hip", "ffn_kernels.h", "wave_tile.h", "moe_internal.h", "device_common.h"):
         with open(os.path.join(ROOT, "expert_grouped_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if rec.get("src_sha256") != h.hexdigest() or workload not in rec:
@@ -295,6 +297,51 @@ def run_decode(args, torch, W):
     return res, roof
 
 
+class _View:
+    """A second call size on a Setup's weights (its first T rows of x)."""
+
+    def __init__(self, S, T):
+        from expert_grouped_quantized_amd.layer import MoELayer
+        self.torch, self.T, self.routed = S.torch, T, S.routed
+        self.x = S.x[:T].contiguous()
+        self.layer = MoELayer(S.desc, S.cfg.k, T)
+        self.layer.set_weights(S.wr, S.routed[0], S.shared, S.bias)
+
+    step = Setup.step
+
+
+def run_bits(args, torch, W):
+    """Every routed code width (2..8 bits, group-32 fp16 scales) on the prefill
+    layer shape: T=4096 eager steps and T=16 as one HIP graph per step."""
+    import dataclasses
+    out = {}
+    for b in (2, 3, 4, 5, 6, 7, 8):
+        fmt = W.I4G32 if b == 4 else W.IG32[b]
+        cfg = dataclasses.replace(W.CONFIGS["int4_T4096"], name=f"bits{b}_T4096", expert=fmt)
+        S = Setup(cfg, cfg.T, torch)
+        wall, layer_ms, per = time_steps(S, args.steps, args.warmup)
+        ms = wall * 1e3 / args.steps
+        act = int((np.diff(S.layer.offsets.cpu().numpy()) > 0).sum())
+        A = algorithmic(cfg, cfg.T, act)
+        D = _View(S, 16)
+        D.step(0)
+        torch.cuda.synchronize()
+        d_act = int((np.diff(D.layer.offsets.cpu().numpy()) > 0).sum())
+        DA = algorithmic(cfg, 16, d_act)
+        g_ms, _ = time_graph(D, args.decode_steps)
+        out[f"{b}bit"] = dict(
+            prefill_tokens_per_s=cfg.T / (ms * 1e-3), prefill_ms=ms, prefill_ffn_ms=per[2],
+            prefill_ffn_tflops=A["ffn_flops"] / (per[2] * 1e-3) / 1e12,
+            decode_graph_tokens_per_s=16 / (g_ms * 1e-3), decode_graph_ms=g_ms,
+            decode_weight_bytes=DA["weight_bytes"],
+            decode_layer_hbm_frac=DA["layer_bytes"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        print(f"[bench] {b}-bit: prefill {ms:.3f} ms (ffn {per[2]:.3f}), decode graph "
+              f"{g_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del S, D
+        torch.cuda.empty_cache()
+    return out
+
+
 def _r(d):
     return {k: (round(v, 4) if isinstance(v, float) else _r(v) if isinstance(v, dict) else v)
             for k, v in d.items()}
@@ -318,6 +365,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "bits":
+        bits = run_bits(args, torch, W)
+        print(json.dumps({"metric": "MoE-layer tokens/s across routed code widths (T=4096 "
+                                    "prefill; T=16 decode as one HIP graph)",
+                          "unit": "tokens/s", "n_gpus": 1, "data": "synthetic",
+                          "config": {"d": 2560, "E": 512, "k": 10, "F": 1024, "n_shared": 1,
+                                     "routed_w": "b-bit symmetric codes, fp16 scale per 32",
+                                     "shared_w": "int8 per-row fp16 scales"},
+                          "bit_widths": _r(bits)}), flush=True)
+        return
     prefill = decode = roof_p = roof_d = pre_inputs = None
     if args.workload in ("both", "prefill"):
         prefill, roof_p, pre_inputs = run_prefill(args, torch, W)
