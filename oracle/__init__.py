@@ -12,7 +12,9 @@ Table 17.1).  This module only marshals numpy arrays into it.
 
 Parity pins (see tests/test_oracle_*.py): brute-force top-k, softmax
 invariants, permutation invariants, the E=1/k=1 dense reduction checked against
-numpy's BLAS product, exhaustive decoder checks, integer-exact cases.
+numpy's BLAS product, exhaustive decoder checks, integer-exact cases; for the
+MXFP4 W4A4 experts the OCP E2M1 table, brute-force rounding, a hand-worked MX
+fixture and perturbation checks of the decision slack.
 """
 from __future__ import annotations
 
@@ -27,10 +29,12 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.environ.get("ORC_LIB_OVERRIDE") or os.path.join(_HERE, "liborc.so")
 
 F32, BF16, I4G32, I8ROW = 0, 1, 2, 3
+MXFP4 = 4  # OCP MX FP4: e2m1 nibbles + E8M0 scale byte per 32 along K (W4A4 experts)
 IG32 = 16  # + b: b-bit symmetric codes, one int8 each, fp16 scale per 32 along K
 I2G32, I3G32, I5G32, I6G32, I7G32, I8G32 = (IG32 + b for b in (2, 3, 5, 6, 7, 8))
 FMT_NAMES = {"f32": F32, "bf16": BF16, "i4g32": I4G32, "i8row": I8ROW, "i2g32": I2G32,
-             "i3g32": I3G32, "i5g32": I5G32, "i6g32": I6G32, "i7g32": I7G32, "i8g32": I8G32}
+             "i3g32": I3G32, "i5g32": I5G32, "i6g32": I6G32, "i7g32": I7G32, "i8g32": I8G32,
+             "mxfp4": MXFP4}
 
 _lib = None
 
@@ -75,8 +79,22 @@ def lib():
         L.orc_swiglu_dense.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
         L.orc_moe_experts.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), i64, vp,
                                       vp, vp, vp, vp, vp]
+        L.orc_moe_experts_mx.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Weights), i64,
+                                         vp, vp, vp, ctypes.c_double, ctypes.c_double, vp, vp,
+                                         vp, vp, vp]
+        L.orc_e2m1_to_f64.argtypes = [i32]
+        L.orc_e2m1_to_f64.restype = ctypes.c_double
+        L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_f64.restype = ctypes.c_double
+        L.orc_e2m1_round.argtypes = [ctypes.c_double]
+        L.orc_e2m1_round.restype = ctypes.c_double
+        L.orc_mx_exponent.argtypes = [ctypes.c_double]
+        L.orc_mx_exponent.restype = ctypes.c_int
+        L.orc_mx_quantize.argtypes = [i64, vp, vp, vp]
+        L.orc_mx_slack.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, vp]
         for fn in ("orc_decode_matrix", "orc_router_logits", "orc_topk_softmax",
-                   "orc_route_plan", "orc_swiglu_dense", "orc_moe_experts"):
+                   "orc_route_plan", "orc_swiglu_dense", "orc_moe_experts",
+                   "orc_moe_experts_mx", "orc_mx_quantize", "orc_mx_slack"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -110,6 +128,51 @@ def bf16_to_f64(bits: int) -> float:
 
 def f16_to_f64(bits: int) -> float:
     return lib().orc_f16_to_f64(int(bits))
+
+
+def e2m1_to_f64(code: int) -> float:
+    """Value of a 4-bit OCP MX e2m1 code."""
+    return lib().orc_e2m1_to_f64(int(code))
+
+
+def e8m0_to_f64(bits: int) -> float:
+    """Value of an OCP MX E8M0 scale byte (NaN for 255)."""
+    return lib().orc_e8m0_to_f64(int(bits))
+
+
+def e2m1_round(y: float) -> float:
+    """Nearest e2m1 value to y, ties to the even mantissa, saturated at +-6."""
+    return lib().orc_e2m1_round(float(y))
+
+
+def mx_exponent(amax: float) -> int:
+    """Shared exponent of an MX block with largest magnitude amax."""
+    return lib().orc_mx_exponent(float(amax))
+
+
+def mx_quantize(v):
+    """OCP MX (FP4) quantization of the rows of v (last dim % 32 == 0), block
+    by block of 32: (dequantized fp64 values, E8M0 scale bytes)."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty_like(v)
+    eb = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    _check(lib().orc_mx_quantize(v.size, _ptr(v), _ptr(out), _ptr(eb)), "mx_quantize")
+    return out, eb
+
+
+def mx_slack(h, dh, wd):
+    """Decision slack of MX(h) against any h' within dh of h (oracle.c,
+    orc_mx_slack): (hq [F], delta [F], slack [d], mag [d]) for wd [d, F]."""
+    h = np.ascontiguousarray(h, np.float64)
+    dh = np.ascontiguousarray(dh, np.float64)
+    wd = np.ascontiguousarray(wd, np.float64)
+    d, F = wd.shape
+    assert h.shape == (F,) and dh.shape == (F,)
+    hq, delta = np.empty(F), np.empty(F)
+    slack, mag = np.empty(d), np.empty(d)
+    _check(lib().orc_mx_slack(d, F, _ptr(h), _ptr(dh), _ptr(wd), _ptr(hq), _ptr(delta),
+                              _ptr(slack), _ptr(mag)), "mx_slack")
+    return hq, delta, slack, mag
 
 
 def router_logits(x, x_fmt, wr, wr_fmt, d, E, bias=None, tokens=None) -> np.ndarray:
@@ -159,6 +222,47 @@ def swiglu_dense(X, wg, wu, wd) -> np.ndarray:
     _check(lib().orc_swiglu_dense(M, d, F, _ptr(X), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(out)),
            "swiglu_dense")
     return out
+
+
+def _layer_args(spec, inputs, ids, w, tokens):
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    n, k = ids.shape[0], spec["k"]
+    assert ids.shape == (n, k) and w.shape == (n, k)
+    D = _Desc(spec["d"], spec["E"], k, spec["F"], spec["n_shared"], spec["Fs"],
+              spec["x_fmt"], spec["expert_fmt"], spec["shared_fmt"])
+    keep = [ids, w]
+
+    def p(name):
+        a = inputs.get(name)
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a.ctypes.data
+
+    W = _Weights(*(p(n_) for n_ in ("x", "wg", "wg_s", "wu", "wu_s", "wd", "wd_s",
+                                    "sg", "sg_s", "su", "su_s", "sd", "sd_s")))
+    tok = None if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    keep.append(tok)
+    return D, W, n, k, tok, ids, w, keep
+
+
+def moe_experts_mx(spec: dict, inputs: dict, ids, w, gamma: float, eta: float, tokens=None):
+    """The layer with MXFP4 W4A4 routed experts, plus the bounds its parity
+    check needs (oracle.c, swiglu_row_mx): returns (y, out_assign, shared_out,
+    slack, mag), the last two [n*k, d] in slot order like out_assign."""
+    D, W, n, k, tok, ids, w, keep = _layer_args(spec, inputs, ids, w, tokens)
+    d = spec["d"]
+    y = np.empty((n, d), np.float64)
+    oa = np.empty((n * k, d), np.float64)
+    so = np.empty((n, d), np.float64) if spec["n_shared"] else None
+    slack = np.empty((n * k, d), np.float64)
+    mag = np.empty((n * k, d), np.float64)
+    _check(lib().orc_moe_experts_mx(ctypes.byref(D), ctypes.byref(W), n, _ptr(tok), _ptr(ids),
+                                    _ptr(w), gamma, eta, _ptr(oa), _ptr(so), _ptr(y),
+                                    _ptr(slack), _ptr(mag)), "moe_experts_mx")
+    return y, oa, so, slack, mag
 
 
 def moe_experts(spec: dict, inputs: dict, ids, w, tokens=None, want_parts: bool = True):

@@ -22,6 +22,9 @@ Recipe (every draw seeded; PCG64 streams keyed by (seed, role[, expert])):
   int8 per row      s = fp16(max|w_row|/127), q = clip(rint(w/s), -127, 127)
   b-bit g32         s = fp16(max|w_group|/(2^(b-1)-1)), q = clip(rint(w/s), +-(2^(b-1)-1)),
                     b = 2, 3, 5, 6, 7, 8 (one int8 per code)
+  mxfp4             E = ceil(log2(max|w_group| / 6)) (E8M0 byte E + 127; 0 for a
+                    zero group), code = the e2m1 magnitude nearest |w| / 2^E
+                    (a midpoint goes to the smaller one) with w's sign
   Zipf bias         bias_e = -c * 1.1 * ln(r_e), r a seeded permutation of 1..E,
                     c = ZIPF_C (chosen so the hottest expert gets about 10x the
                     mean load on the seeded T=16384 input).
@@ -38,6 +41,8 @@ F32, BF16, I4G32, I8ROW = "f32", "bf16", "i4g32", "i8row"
 # b-bit group-32 formats: symmetric codes, one int8 each, fp16 scale per 32 along K
 IG32 = {2: "i2g32", 3: "i3g32", 5: "i5g32", 6: "i6g32", 7: "i7g32", 8: "i8g32"}
 IG32_BITS = {v: b for b, v in IG32.items()}
+# OCP MX FP4 (e2m1 codes + E8M0 scale per 32 along K), W4A4 routed experts
+MXFP4 = "mxfp4"
 ZIPF_S = 1.1
 ZIPF_C = 0.22
 
@@ -55,7 +60,7 @@ class LayerConfig:
     Fs: int
     act: str          # hidden / output dtype: f32 | bf16
     router: str       # router weight dtype: f32 | bf16
-    expert: str       # routed expert weights: f32 | bf16 | i4g32
+    expert: str       # routed expert weights: f32 | bf16 | i4g32 | i{2..8}g32 | mxfp4
     shared: str       # shared expert weights: f32 | bf16 | i8row
     zipf: bool = False
     extra_T: tuple = field(default_factory=tuple)
@@ -133,6 +138,26 @@ def quantize_ig32(w: np.ndarray, b: int):
     return q, s16.view(np.uint16)
 
 
+# e2m1 magnitudes by code (bits 2..0) and the midpoints between neighbours
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """[rows, K] float -> (packed e2m1 uint8 [rows, K/2], E8M0 uint8 [rows, K/32])."""
+    rows, K = w.shape
+    assert K % 32 == 0
+    g = w.reshape(rows, K // 32, 32).astype(np.float64)
+    amax = np.abs(g).max(axis=2)
+    m, ex = np.frexp(amax / 6.0)                   # amax/6 = m 2^ex, m in [0.5, 1)
+    E = np.where(amax > 0, ex - (m == 0.5), -127)  # ceil(log2(amax / 6))
+    E = np.clip(E, -127, 127)
+    a = np.abs(g) / np.ldexp(1.0, E)[..., None]
+    code = np.searchsorted(_E2M1_MID, a, side="left").astype(np.uint8)
+    code |= np.where((g < 0) & (code > 0), 8, 0).astype(np.uint8)
+    code = code.reshape(rows, K)
+    return (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8), (E + 127).astype(np.uint8)
+
+
 def quantize_i8row(w: np.ndarray):
     """[rows, K] float -> (int8 [rows, K], fp16 bits [rows])."""
     w = w.astype(np.float32)
@@ -155,6 +180,8 @@ def store(w: np.ndarray, fmt: str):
         return quantize_i8row(w)
     if fmt in IG32_BITS:
         return quantize_ig32(w, IG32_BITS[fmt])
+    if fmt == MXFP4:
+        return quantize_mxfp4(w)
     raise ValueError(fmt)
 
 
