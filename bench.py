@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense fp4 (MXFP4) MFMA, TFLOP/s
 N_ROT = 4                    # routed-blob copies rotated across steps
 
 
@@ -40,7 +41,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
-    p.add_argument("--workload", choices=("both", "prefill", "decode", "bits"), default="both",
+    p.add_argument("--workload", choices=("both", "prefill", "decode", "bits", "mxfp4"),
+                   default="both",
                    help="limit the run to one workload (for per-workload profiles)")
     return p.parse_args()
 
@@ -173,7 +175,7 @@ def algorithmic(cfg, T, n_active):
     """Flops and bytes of one layer call (the definition, not what the kernels move)."""
     d, F, Fs, k, E = cfg.d, cfg.F, cfg.Fs, cfg.k, cfg.E
     import workloads as W
-    wbytes = {"i4g32": 0.5 + 2 / 32, "bf16": 2.0, "i8row": 1.0}
+    wbytes = {"i4g32": 0.5 + 2 / 32, "bf16": 2.0, "i8row": 1.0, "mxfp4": 0.5 + 1 / 32}
     wbytes.update({name: b / 8 + 2 / 32 for b, name in W.IG32.items()})
     ffn_flops = 6.0 * T * k * d * F + 6.0 * T * d * Fs
     router_flops = 2.0 * T * E * d
@@ -181,9 +183,13 @@ def algorithmic(cfg, T, n_active):
     shared = 3 * d * Fs * wbytes[cfg.shared] + (2 * Fs + d) * 2 * (cfg.shared == "i8row")
     weight_bytes = n_active * per_expert + shared
     act = T * d * 2 * 2 + E * d * 2                     # x in, y out, router weights
-    # h (bf16) written and read back; per-assignment and shared outputs (fp32)
-    # written by the down products and read by the combine
-    inter = T * k * F * 2 * 2 + T * Fs * 2 * 2 + T * k * d * 4 * 2 + T * d * 4 * 2
+    # h written and read back (bf16; MXFP4 layers: e2m1 codes + E8M0 scales,
+    # and x's codes written and read once); per-assignment and shared outputs
+    # (fp32) written by the down products and read by the combine
+    mx = cfg.expert == W.MXFP4
+    hb = 0.5 + 1 / 32 if mx else 2.0
+    inter = (T * k * F * hb * 2 + T * Fs * 2 * 2 + T * k * d * 4 * 2 + T * d * 4 * 2
+             + (T * d * hb * 2 if mx else 0))
     return dict(ffn_flops=ffn_flops, router_flops=router_flops, weight_bytes=weight_bytes,
                 ffn_bytes=weight_bytes + T * d * 2 + inter - T * d * 4 - T * k * d * 4,
                 layer_bytes=weight_bytes + act + inter)
@@ -342,6 +348,55 @@ def run_bits(args, torch, W):
     return out
 
 
+def run_mxfp4(args, torch, W):
+    """MXFP4 W4A4 routed experts (scaled FP4 MFMA) on the prefill layer shape:
+    T=4096 eager steps; its first 16 rows as eager steps and as one HIP graph
+    per step; its first 32 rows as a graph."""
+    import dataclasses
+    cfg = dataclasses.replace(W.CONFIGS["int4_T4096"], name="mxfp4_T4096", expert=W.MXFP4)
+    S = Setup(cfg, cfg.T, torch)
+    wall, layer_ms, per = time_steps(S, args.steps, args.warmup)
+    ms = wall * 1e3 / args.steps
+    act = int((np.diff(S.layer.offsets.cpu().numpy()) > 0).sum())
+    A = algorithmic(cfg, cfg.T, act)
+    ffn_s = per[2] * 1e-3
+    pre = dict(T=cfg.T, tokens_per_s=cfg.T / (ms * 1e-3), ms_per_step=ms, layer_event_ms=layer_ms,
+               call_ms=dict(route=per[0], permute=per[1], grouped_ffn=per[2], combine=per[3]),
+               active_experts=act,
+               ffn_tflops=A["ffn_flops"] / ffn_s / 1e12,
+               ffn_fp4_mfma_frac=A["ffn_flops"] / ffn_s / 1e12 / FP4_PEAK_TFLOPS,
+               ffn_algorithmic_bytes=A["ffn_bytes"],
+               ffn_gbs=A["ffn_bytes"] / ffn_s / 1e9,
+               ffn_hbm_frac=A["ffn_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS)
+    out = {"prefill": pre}
+    for T in (16, 32):
+        D = _View(S, T)
+        D.step(0)
+        torch.cuda.synchronize()
+        d_act = int((np.diff(D.layer.offsets.cpu().numpy()) > 0).sum())
+        DA = algorithmic(cfg, T, d_act)
+        rec = dict(T=T, active_experts=d_act, weight_bytes=DA["weight_bytes"])
+        if T == 16:
+            dwall, dlayer, dper = time_steps(D, args.decode_steps, 10)
+            d_ms = dwall * 1e3 / args.decode_steps
+            rec.update(tokens_per_s=T / (d_ms * 1e-3), ms_per_step=d_ms, layer_event_ms=dlayer,
+                       call_ms=dict(route=dper[0], permute=dper[1], grouped_ffn=dper[2],
+                                    combine=dper[3]),
+                       ffn_weight_gbs=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9,
+                       ffn_weight_hbm_frac=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        g_ms, g_ev = time_graph(D, args.decode_steps)
+        rec["graph"] = dict(ms_per_step=g_ms, event_ms_per_step=g_ev, tokens_per_s=T / (g_ms * 1e-3),
+                            layer_hbm_frac=DA["layer_bytes"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        out[f"decode_T{T}"] = rec
+        print(f"[bench] mxfp4 T={T}: graph {g_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del D
+        torch.cuda.empty_cache()
+    print(f"[bench] mxfp4 T=4096: {ms:.3f} ms (ffn {per[2]:.3f} ms)", file=sys.stderr, flush=True)
+    del S
+    torch.cuda.empty_cache()
+    return out
+
+
 def _r(d):
     return {k: (round(v, 4) if isinstance(v, float) else _r(v) if isinstance(v, dict) else v)
             for k, v in d.items()}
@@ -374,6 +429,19 @@ def main():
                                      "routed_w": "b-bit symmetric codes, fp16 scale per 32",
                                      "shared_w": "int8 per-row fp16 scales"},
                           "bit_widths": _r(bits)}), flush=True)
+        return
+    if args.workload == "mxfp4":
+        mx = run_mxfp4(args, torch, W)
+        print(json.dumps({"metric": "MoE-layer tokens/s with MXFP4 W4A4 routed experts (T=4096 "
+                                    "prefill; T=16 and T=32 decode)",
+                          "unit": "tokens/s", "n_gpus": 1, "data": "synthetic", "dtype": "fp4",
+                          "config": {"workload": "moe_layer_mxfp4_w4a4", "d": 2560, "E": 512,
+                                     "k": 10, "F": 1024, "n_shared": 1,
+                                     "routed_w": "MXFP4 (e2m1 + E8M0 per 32), activations "
+                                                 "MXFP4-quantized per 32",
+                                     "shared_w": "int8 per-row fp16 scales, bf16 activations"},
+                          "peaks": {"fp4_mfma_tflops": FP4_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS},
+                          "mxfp4": _r(mx)}), flush=True)
         return
     prefill = decode = roof_p = roof_d = pre_inputs = None
     if args.workload in ("both", "prefill"):

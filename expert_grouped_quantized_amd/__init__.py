@@ -16,10 +16,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EDEVICE = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_I4_G32, MOE_I8_ROW = 0, 1, 2, 3
 MOE_I2_G32, MOE_I3_G32, MOE_I5_G32, MOE_I6_G32, MOE_I7_G32, MOE_I8_G32 = 4, 5, 6, 7, 8, 9
+MOE_MXFP4 = 10
 MOE_BLOB_ROUTED, MOE_BLOB_SHARED = 0, 1
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "i4g32": MOE_I4_G32, "i8row": MOE_I8_ROW,
           "i2g32": MOE_I2_G32, "i3g32": MOE_I3_G32, "i5g32": MOE_I5_G32, "i6g32": MOE_I6_G32,
-          "i7g32": MOE_I7_G32, "i8g32": MOE_I8_G32}
+          "i7g32": MOE_I7_G32, "i8g32": MOE_I8_G32, "mxfp4": MOE_MXFP4}
 
 
 class MoeError(RuntimeError):

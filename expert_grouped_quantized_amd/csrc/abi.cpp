@@ -50,9 +50,10 @@ moe_status check_desc(const moe_desc* D) {
     if (D->d % 64 || D->ffn % 64 || (D->n_shared && D->shared_ffn % 64))
       return fail(MOE_EUNSUPPORTED, "F32 path needs d, ffn, shared_ffn multiples of 64");
   } else if (D->act == MOE_BF16) {
-    if (D->expert_w != MOE_BF16 && ig32_bits(D->expert_w) == 0)
+    if (D->expert_w != MOE_BF16 && ig32_bits(D->expert_w) == 0 && D->expert_w != MOE_MXFP4)
       return fail(MOE_EUNSUPPORTED,
-                  "act BF16 needs routed weights BF16, I4_G32 or I{2,3,5,6,7,8}_G32 (got %d)",
+                  "act BF16 needs routed weights BF16, I4_G32, I{2,3,5,6,7,8}_G32 or MXFP4 "
+                  "(got %d)",
                   D->expert_w);
     if (D->n_shared && D->shared_w != MOE_BF16 && D->shared_w != MOE_I8_ROW)
       return fail(MOE_EUNSUPPORTED, "act BF16 needs shared weights BF16 or I8_ROW (got %d)",
@@ -60,9 +61,13 @@ moe_status check_desc(const moe_desc* D) {
     if (D->d % OUT_COLS_BLOCK || D->ffn % H_COLS_BLOCK ||
         (D->n_shared && D->shared_ffn % H_COLS_BLOCK))
       return fail(MOE_EUNSUPPORTED, "BF16 path needs d %% 256 == 0 and ffn, shared_ffn %% 128 == 0");
-    if (D->ffn % (KC * lead_of(D->expert_w, LEAD_I4)))
+    const int kstep = kc_of(D->expert_w) * lead_of(D->expert_w, LEAD_I4);
+    if (D->ffn % kstep || D->d % kstep) {
+      if (D->expert_w == MOE_MXFP4)
+        return fail(MOE_EUNSUPPORTED, "MXFP4 routed experts need d, ffn %% %d == 0", kstep);
       return fail(MOE_EUNSUPPORTED, "%d-bit routed experts need ffn %% %d == 0",
-                  ig32_bits(D->expert_w), KC * lead_of(D->expert_w, LEAD_I4));
+                  ig32_bits(D->expert_w), kstep);
+    }
   } else {
     return fail(MOE_EUNSUPPORTED, "act dtype %d unsupported", D->act);
   }
@@ -171,9 +176,32 @@ bool pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* 
   return true;
 }
 
+// MXFP4 tile (64 rows x 128 K, for the scaled FP4 MFMA 16x16x128): lane l of
+// the consuming wave takes row c = l % 16 of each fragment and the 32-K block
+// kb = l / 16 of the chunk.  Fragment f's 16 code bytes of lane l (the
+// canonical bytes of that row and block, element 2j in the low nibble) at
+// f*1024 + l*16; lane l's four E8M0 scales (byte f = fragment f) at
+// 4096 + l*4.  Returns false on a NaN (255) scale.
+template <typename RowOf>
+bool pack_tile_mx(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
+  for (int lane = 0; lane < 64; lane++) {
+    const int kb = lane >> 4;
+    for (int f = 0; f < 4; f++) {
+      const MatIO& M = *m[f];
+      const int64_t r = row_of(f, lane & 15);
+      memcpy(dst + f * 1024 + lane * 16, M.q + r * (M.K / 2) + kc * (KC_MX / 2) + kb * 16, 16);
+      const uint8_t sc = M.s[r * (M.K / 32) + kc * 4 + kb];
+      if (sc == 255) return false;
+      dst[4096 + lane * 4 + f] = sc;
+    }
+  }
+  return true;
+}
+
 template <typename RowOf>
 bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   const int fmt = m[0]->fmt;
+  if (fmt == MOE_MXFP4) return pack_tile_mx(m, row_of, kc, dst);
   if (fmt != MOE_I4_G32 && ig32_bits(fmt) != 0) return pack_tile_ig32(m, row_of, kc, dst);
   for (int f = 0; f < 4; f++) {
     const MatIO& M = *m[f];
@@ -236,9 +264,23 @@ void unpack_tile_ig32(const MatIO* const m[4], const OutIO out[4], RowOf row_of,
 }
 
 template <typename RowOf>
+void unpack_tile_mx(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int64_t kc,
+                    const uint8_t* src) {
+  for (int lane = 0; lane < 64; lane++) {
+    const int kb = lane >> 4;
+    for (int f = 0; f < 4; f++) {
+      const int64_t r = row_of(f, lane & 15), K = m[f]->K;
+      memcpy(out[f].q + r * (K / 2) + kc * (KC_MX / 2) + kb * 16, src + f * 1024 + lane * 16, 16);
+      out[f].s[r * (K / 32) + kc * 4 + kb] = src[4096 + lane * 4 + f];
+    }
+  }
+}
+
+template <typename RowOf>
 void unpack_tile(const MatIO* const m[4], const OutIO out[4], RowOf row_of, int64_t kc,
                  const uint8_t* src) {
   const int fmt = m[0]->fmt;
+  if (fmt == MOE_MXFP4) return unpack_tile_mx(m, out, row_of, kc, src);
   if (fmt != MOE_I4_G32 && ig32_bits(fmt) != 0) return unpack_tile_ig32(m, out, row_of, kc, src);
   for (int f = 0; f < 4; f++) {
     const int64_t K = m[f]->K;
@@ -279,11 +321,14 @@ size_t canon_q_bytes(int fmt, int64_t rows, int64_t K) {
     case MOE_F32: return rows * K * 4;
     case MOE_BF16: return rows * K * 2;
     case MOE_I4_G32: return rows * K / 2;
+    case MOE_MXFP4: return rows * K / 2;
     default: return rows * K;
   }
 }
 size_t canon_s_bytes(int fmt, int64_t rows, int64_t K) {
-  return ig32_bits(fmt) ? rows * (K / 32) * 2 : fmt == MOE_I8_ROW ? rows * 2 : 0;
+  return ig32_bits(fmt) ? rows * (K / 32) * 2
+       : fmt == MOE_I8_ROW ? rows * 2
+       : fmt == MOE_MXFP4 ? rows * (K / 32) : 0;
 }
 
 struct ExpertIO {  // canonical pointers of one expert (gate, up, down)
@@ -307,7 +352,7 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
     return true;
   }
   const size_t tb = tile_bytes(fmt);
-  const int64_t nk1 = d / KC, nk2 = F / KC;
+  const int64_t nk1 = d / kc_of(fmt), nk2 = F / kc_of(fmt);
   const MatIO G{fmt, F, d, io.g, io.gs}, U{fmt, F, d, io.u, io.us}, Dn{fmt, d, F, io.dn, io.ds};
   // W1 run j (h columns c0 = 32*j): fragments 0, 1 = gate rows c0 + 16*(f%2) + c,
   // fragments 2, 3 = up rows of the same columns; runs in order, then K chunks
@@ -372,7 +417,7 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
   const int64_t d = D->d, F = kind == MOE_BLOB_ROUTED ? D->ffn : D->shared_ffn;
   const size_t need = n * expert_bytes(fmt, d, F);
   if (!blob || !gate || !up || !down) return fail(MOE_EINVAL, "NULL weight or blob pointer");
-  if ((ig32_bits(fmt) || fmt == MOE_I8_ROW) && (!gs || !us || !ds))
+  if ((ig32_bits(fmt) || fmt == MOE_I8_ROW || fmt == MOE_MXFP4) && (!gs || !us || !ds))
     return fail(MOE_EINVAL, "quantized weights need their scales");
   if (blob_bytes < need) return fail(MOE_EINVAL, "blob_bytes %zu < %zu", blob_bytes, need);
   const size_t gq = canon_q_bytes(fmt, F, d), gsb = canon_s_bytes(fmt, F, d);
@@ -393,6 +438,9 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
   for (auto& t : th) t.join();
   for (int64_t e = 0; e < n; e++)
     if (bad[e]) {
+      if (fmt == MOE_MXFP4)
+        return fail(MOE_EINVAL, "expert %lld holds an MXFP4 scale byte of 255 (NaN)",
+                    (long long)e);
       const int b = ig32_bits(fmt);
       return fail(MOE_EINVAL, "expert %lld holds a code outside [%d, %d]", (long long)e,
                   -((1 << (b - 1)) - 1), (1 << (b - 1)) - 1);
@@ -542,6 +590,8 @@ moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* 
   a.shared_blob = (const uint8_t*)shared_blob;
   a.h_routed = w + L.h_routed; a.h_shared = w + L.h_shared;
   a.x16 = (uint16_t*)(w + L.x16); a.xscale = (float*)(w + L.xexp);
+  a.xq = w + L.x16; a.xsc = w + L.xexp;
+  a.hq = w + L.h_routed; a.hsc = w + L.h_scale;
   a.out_assign = out_assign; a.shared_out = shared_out;
   hipStream_t s = (hipStream_t)stream;
   return device_result(D->act == MOE_F32 ? launch_ffn_f32(a, s) : launch_ffn_bf16(a, s),

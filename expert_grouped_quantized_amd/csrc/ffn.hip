@@ -63,6 +63,7 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   if (a.routed_fmt == MOE_I4_G32 && sf == MOE_I8_ROW)
     return launch_pair<MOE_I4_G32, MOE_I8_ROW>(a, s);
   if (ig32_bits(a.routed_fmt) != 0) return launch_ffn_lowbit(a, s);
+  if (a.routed_fmt == MOE_MXFP4) return launch_ffn_mx(a, s);
   return hipErrorInvalidValue;
 }
 

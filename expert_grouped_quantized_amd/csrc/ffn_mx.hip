@@ -1,0 +1,397 @@
+// ffn_mx.hip -- expert-grouped SwiGLU GEMMs of MXFP4 W4A4 routed experts
+// ("anvil-serving" dossier, Qwen3.8-Flash-Next entry, section "Quantization
+// boundary": 4-bit weights and activations on the routed experts, the shared
+// expert 16-bit), in the OCP Microscaling FP4 format that CDNA4's scaled
+// MFMA (16x16x128, e2m1 operands, one E8M0 scale per 32 K per row) consumes.
+//
+//   x_to_mx_kernel   each token row of x -> e2m1 codes + E8M0 scales, block by
+//                    block of 32 (OCP MX rule), into the workspace
+//   ffn_mx_kernel<1> routed tiles: g, u = Wg xq, Wu xq on the FP4 MFMA;
+//                    h = w * silu(g) * u in fp32, quantized per row and 32 h
+//                    columns (one wave's columns) -> hq, hsc
+//   ffn_mx_kernel<2> routed tiles: out_assign = Wd hq on the FP4 MFMA
+// Shared-expert tiles of the same launches run the 16-bit path of
+// ffn_kernels.h on the unquantized bf16 x.
+//
+// Work unit and grid as in ffn_kernels.h (row tile of up to 16 * MAXMF rows x
+// one column block of 4 waves; each wave one run of 64 weight rows).  A K
+// chunk is 128: per chunk a wave reads one 4352-byte weight tile (4 fragments
+// x 16 bytes of codes + one scale dword per lane) straight into registers,
+// and the block stages the tile rows' codes (64 bytes a row) and scales
+// through LDS, double-buffered.  No dequantization: codes and scales feed the
+// MFMA as they are.
+#include <utility>
+
+#include "ffn_kernels.h"
+
+namespace moe {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
+  (fn(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
+
+// acc += A (16 rows x 128 K) * B (16 columns x 128 K)^T, e2m1 operands.  Lane
+// l supplies row / column l % 16 and K block l / 16 (32 codes, element 2j in
+// the low nibble of byte j); byte OA of sa is the E8M0 scale of its A block,
+// byte OB of sb that of its B block.  The result layout is the 16x16x32 one.
+template <int OA, int OB>
+__device__ __forceinline__ f32x4_t mfma_fp4(const u32x4_t& a, uint32_t sa, const u32x4_t& b,
+                                            uint32_t sb, f32x4_t c) {
+  const i32x8_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, OA, (int)sa, OB,
+                                                          (int)sb);
+}
+
+// Two fp32 values, already divided by their block scale, to two e2m1 codes
+// (nearest, ties to even, saturated at +-6) in byte SEL of `old` (the first
+// value in the low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Shared exponent of an MX block from the bits of its largest magnitude:
+// floor(log2 amax) - 2, clamped to [-127, 127] (-127 for zero and subnormal
+// maxima).  Returns E; *inv = 2^-E (a normal float for every such E).
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits, float* inv) {
+  const int E = max((int)(amax_bits >> 23) - 129, -127);
+  *inv = __uint_as_float((uint32_t)(127 - E) << 23);
+  return E;
+}
+
+// ---- x -> MXFP4 --------------------------------------------------------------
+// One thread per 32-element block of a row: 64 bytes of bf16 in, 16 bytes of
+// codes and one scale byte out.
+__global__ __launch_bounds__(256) void x_to_mx_kernel(int T, int d, const uint16_t* __restrict__ x,
+                                                      uint8_t* __restrict__ xq,
+                                                      uint8_t* __restrict__ xsc) {
+  const int nb = d / 32;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)T * nb) return;
+  const int64_t t = g / nb;
+  const int b = (int)(g - t * nb);
+  const u32x4_t* src = (const u32x4_t*)(x + t * d + b * 32);
+  u32x4_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) v[j] = src[j];
+  uint32_t m = 0;  // largest |x| as float bits
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int w = 0; w < 4; w++) m = max(m, max((v[j][w] << 16) & 0x7fffffffu, v[j][w] & 0x7fff0000u));
+  float inv;
+  const int E = mx_exponent(m, &inv);
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    // dword w of piece j holds elements 8j + 2w (low half) and 8j + 2w + 1
+    uint32_t c = 0;
+    c = cvt_fp4x2<0>(c, bf16_lo(v[j][0]) * inv, bf16_hi(v[j][0]) * inv);
+    c = cvt_fp4x2<1>(c, bf16_lo(v[j][1]) * inv, bf16_hi(v[j][1]) * inv);
+    c = cvt_fp4x2<2>(c, bf16_lo(v[j][2]) * inv, bf16_hi(v[j][2]) * inv);
+    c = cvt_fp4x2<3>(c, bf16_lo(v[j][3]) * inv, bf16_hi(v[j][3]) * inv);
+    o[j] = c;
+  }
+  *(u32x4_t*)(xq + t * (d / 2) + b * 16) = o;
+  xsc[t * nb + b] = (uint8_t)(E + 127);
+}
+
+// ---- weight registers of one MXFP4 wave tile (64 rows x 128 K) -------------
+struct WTileMx {
+  u32x4_t v[4];  // fragment f: the lane's 32 codes (row l % 16, K block l / 16)
+  uint32_t sc;   // byte f: the E8M0 scale of fragment f's row and block
+  template <bool NT>
+  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+#pragma unroll
+    for (int f = 0; f < 4; f++) v[f] = ldw<NT>(t + f * 1024, lane);
+    const uint32_t* sp = (const uint32_t*)(t + 4096) + lane;
+    sc = NT ? __builtin_nontemporal_load(sp) : *sp;
+  }
+};
+
+// Activation rows of one 128-K chunk in LDS: 64 code bytes a row as four
+// 16-byte pieces, piece kb of row r at slot kb ^ swz(r), so the pieces that 8
+// (or 16) consecutive rows read at one kb, and that 16 consecutive pieces
+// write, fall in distinct 16-byte bank groups.  The scales sit apart as
+// [kb][r % 16][r / 16] bytes: a lane reads the scales of all its row
+// fragments with one 8-byte load.
+__device__ __forceinline__ int mx_lds_index(int row, int kb) {
+  const int swz = ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  return row * 64 + ((kb ^ swz) << 4);
+}
+
+template <int MAXMF>
+struct SmemMx {
+  uint8_t a[2][MAXMF * 16 * 64];
+  uint8_t s[2][4 * 16 * 8];
+  float wrow[MAXMF * 16];
+  int src[MAXMF * 16];
+};
+
+// Stage-1 epilogue: h = w * silu(g) * u of the wave's 32 h columns, quantized
+// to MXFP4 per row (the 32 columns are one block), codes into hq (row-major,
+// F/2 bytes a row) and scales into hsc (F/32 bytes a row).  Row
+// i*16 + 4*(lane/16) + r of the tile holds, in lane l, column 16 f + l % 16
+// for f = 0, 1 (gate fragments f, up fragments f + 2).  The row maximum runs
+// over the 16 lanes of a DPP row; lanes l and l^1 then trade their codes and
+// each writes whole bytes (two columns) of two rows.
+template <int NMF, typename RowW>
+__device__ __forceinline__ void store_h_mx(const FfnArgs& A, int start, int cnt, int run,
+                                           const f32x4_t (&acc)[NMF][4], RowW wrow) {
+  const int lane = threadIdx.x & 63, c = lane & 15, quad = 4 * (lane >> 4);
+  const bool odd = lane & 1;
+  const size_t qs = (size_t)A.F / 2, ss = (size_t)A.F / 32;
+  uint8_t* hq = A.hq + (size_t)start * qs + run * 16 + (c >> 1);
+  uint8_t* hs = A.hsc + (size_t)start * ss + run;
+#pragma unroll
+  for (int i = 0; i < NMF; i++) {
+    float h0[4], h1[4];
+    uint32_t eb[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float w = wrow(i, r);
+      h0[r] = w * silu_fast(acc[i][0][r]) * acc[i][2][r];
+      h1[r] = w * silu_fast(acc[i][1][r]) * acc[i][3][r];
+      uint32_t m = max(__float_as_uint(h0[r]) & 0x7fffffffu, __float_as_uint(h1[r]) & 0x7fffffffu);
+      // max over the 16 lanes of the DPP row: quad_perm [1,0,3,2], [2,3,0,1],
+      // then row_half_mirror and row_mirror
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x140, 0xF, 0xF, false));
+      float inv;
+      eb[r] = (uint32_t)(mx_exponent(m, &inv) + 127);
+      h0[r] *= inv;
+      h1[r] *= inv;
+    }
+    // nibble 4 f + r = the code of (row r, fragment f)
+    uint32_t code = 0;
+    code = cvt_fp4x2<0>(code, h0[0], h0[1]);
+    code = cvt_fp4x2<1>(code, h0[2], h0[3]);
+    code = cvt_fp4x2<2>(code, h1[0], h1[1]);
+    code = cvt_fp4x2<3>(code, h1[2], h1[3]);
+    const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, 0xB1, 0xF, 0xF, false);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int r = odd ? 2 + q : q;  // the even lane writes rows 0, 1, the odd lane 2, 3
+      const int row = i * 16 + quad + r;
+#pragma unroll
+      for (int f = 0; f < 2; f++) {
+        const int n = 4 * (4 * f + r);
+        const uint32_t mine = (code >> n) & 15u, oth = (other >> n) & 15u;
+        const uint32_t byte = odd ? (oth | (mine << 4)) : (mine | (oth << 4));
+        if (row < cnt) hq[(size_t)row * qs + 8 * f] = (uint8_t)byte;
+      }
+    }
+    if (c < 4) {
+      const int row = i * 16 + quad + c;
+      const uint32_t e = c == 0 ? eb[0] : c == 1 ? eb[1] : c == 2 ? eb[2] : eb[3];
+      if (row < cnt) hs[(size_t)row * ss] = (uint8_t)e;
+    }
+  }
+}
+
+// One routed (row tile, column block) of an MXFP4 layer.
+template <int STAGE, int MAXMF, int PF, bool NT>
+__device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, SmemMx<MAXMF>& sm) {
+  constexpr int NMF = MAXMF;
+  constexpr int ROWS = MAXMF * 16;
+  constexpr int PIECES = ROWS * 4;  // 16-byte code pieces of one chunk
+  constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
+  static_assert(PPT <= 2, "code staging holds at most 2 pieces per thread");
+  static_assert(PF == 2 || PF == 4, "load lead must be 2 or 4 chunks");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = STAGE == 1 ? A.d : A.F;
+  const int nk = K / KC_MX;
+  const int run = J.nb * WAVES + wave;
+  const uint8_t* blob = A.routed_blob + (size_t)J.expert * expert_bytes(MOE_MXFP4, A.d, A.F);
+  const uint8_t* sect = STAGE == 1 ? blob : blob + w1_bytes(MOE_MXFP4, A.d, A.F);
+  const uint8_t* wnext = sect + (size_t)run * nk * TILE_BYTES_MX4;
+
+  for (int m = tid; m < ROWS; m += WAVES * 64) {
+    int src = -1;
+    float wf = 0.0f;
+    if (m < J.cnt) {
+      if (STAGE == 1) {
+        const int f = A.perm[J.start + m];
+        src = f / A.k;
+        wf = A.topk_w[f];
+      } else {
+        src = J.start + m;
+      }
+    }
+    sm.src[m] = src;
+    sm.wrow[m] = wf;
+  }
+  __syncthreads();
+
+  // Rows past the tile's end read the tile's first row (never stored).
+  const uint8_t* qbase = STAGE == 1 ? A.xq : A.hq;
+  const uint8_t* sbase = STAGE == 1 ? A.xsc : A.hsc;
+  const size_t qstride = (size_t)K / 2, sstride = (size_t)K / 32;
+  const uint8_t* aq[PPT];
+  int aq_lds[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; j++) {
+    const int q = (tid + WAVES * 64 * j) % PIECES;  // piece q: row q / 4, K block q % 4
+    const int r = q >> 2, kb = q & 3;
+    const int s = sm.src[r] >= 0 ? sm.src[r] : sm.src[0];
+    aq[j] = qbase + (size_t)s * qstride + kb * 16;
+    aq_lds[j] = mx_lds_index(r, kb);
+  }
+  // scales: thread tid stages row tid % ROWS (4 bytes a chunk)
+  const int srow = tid % ROWS;
+  const uint8_t* as;
+  {
+    const int s = sm.src[srow] >= 0 ? sm.src[srow] : sm.src[0];
+    as = sbase + (size_t)s * sstride;
+  }
+  const int s_lds = (srow & 15) * 8 + (srow >> 4);  // + kb * 128
+
+  f32x4_t acc[NMF][4];
+#pragma unroll
+  for (int i = 0; i < NMF; i++)
+#pragma unroll
+    for (int f = 0; f < 4; f++) acc[i][f] = f32x4_t{0, 0, 0, 0};
+
+  u32x4_t areg[PF][PPT];
+  uint32_t asreg[PF];
+  auto load_a = [&](int kc, int p) {
+#pragma unroll
+    for (int j = 0; j < PPT; j++) areg[p][j] = *(const u32x4_t*)(aq[j] + kc * (KC_MX / 2));
+    asreg[p] = *(const uint32_t*)(as + kc * 4);
+  };
+  auto store_a = [&](int buf, int p) {
+#pragma unroll
+    for (int j = 0; j < PPT; j++) *(u32x4_t*)(sm.a[buf] + aq_lds[j]) = areg[p][j];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) sm.s[buf][kb * 128 + s_lds] = (uint8_t)(asreg[p] >> (8 * kb));
+  };
+  const int am = lane & 15, akb = lane >> 4;
+  auto compute = [&](int buf, const WTileMx& w) {
+    u32x4_t av[NMF];
+#pragma unroll
+    for (int i = 0; i < NMF; i++) av[i] = *(const u32x4_t*)(sm.a[buf] + mx_lds_index(i * 16 + am, akb));
+    uint32_t sa[2];
+    if constexpr (NMF > 4) {
+      const uint2 t = *(const uint2*)(sm.s[buf] + akb * 128 + am * 8);
+      sa[0] = t.x;
+      sa[1] = t.y;
+    } else {
+      sa[0] = *(const uint32_t*)(sm.s[buf] + akb * 128 + am * 8);
+      sa[1] = 0;
+    }
+    static_for<4>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      static_for<NMF>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        acc[i][f] = mfma_fp4<i & 3, f>(av[i], sa[i >> 2], w.v[f], w.sc, acc[i][f]);
+      });
+    });
+  };
+
+  // The peeled pipeline of ffn_kernels.h's tile_body: step kc issues the
+  // activation and weight loads of chunk kc + PF in the order they are
+  // waited for; nk is a multiple of PF (the ABI's width checks).
+  WTileMx ring[PF];
+#pragma unroll
+  for (int p = 0; p < PF; p++) {
+    load_a(p, p);
+    ring[p].template load<NT>(wnext, lane);
+    wnext += TILE_BYTES_MX4;
+  }
+  store_a(0, 0);
+  __syncthreads();
+  for (int kc0 = 0; kc0 < nk - PF; kc0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; p++) {
+      load_a(kc0 + p + PF, p);  // set p held chunk kc0 + p, already in LDS
+      compute(p & 1, ring[p]);
+      ring[p].template load<NT>(wnext, lane);
+      wnext += TILE_BYTES_MX4;
+      store_a((p + 1) & 1, (p + 1) % PF);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; p++) {
+    compute(p & 1, ring[p]);
+    if (p + 1 < PF) {
+      store_a((p + 1) & 1, p + 1);
+      __syncthreads();
+    }
+  }
+
+  const int quad = 4 * (lane >> 4);
+  auto wrow = [&](int i, int r) { return sm.wrow[i * 16 + quad + r]; };
+  if constexpr (STAGE == 1) {
+    store_h_mx<NMF>(A, J.start, J.cnt, run, acc, wrow);
+  } else {
+    store_wave_tile<MOE_MXFP4, 2, NMF, false>(A, false, J.start, J.cnt, run, A.F, sect, acc, wrow,
+                                               [](int, int) { return 1.0f; });
+  }
+}
+
+template <int SF, int STAGE, int MAXMF, int PF>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_mx_kernel(FfnArgs A) {
+  __shared__ __attribute__((aligned(16))) union {
+    Smem<MAXMF> b;
+    SmemMx<MAXMF> m;
+  } sm;
+  const int nr = STAGE == 1 ? col_blocks(A.F / H_COLS_WAVE) : col_blocks(A.d / OUT_COLS_WAVE);
+  const int ns = STAGE == 1 ? (A.n_shared ? col_blocks(A.Fs / H_COLS_WAVE) : 0) : nr;
+  TileJob J;
+  if (!decode_job(A, max(nr, ns), nr, ns, MAXMF * 16, J)) return;
+  // Routed weights stream past the caches at every call size (measured: at
+  // T=4096 the few experts whose rows span two tiles re-read theirs, and
+  // still the layer is faster than with cacheable loads).
+  constexpr bool NT_ROUTED = true;
+  if (J.shared)
+    run_tile<SF, STAGE, MAXMF, LEAD_I4, false, false>(A, J, sm.b);
+  else
+    run_tile_mx<STAGE, MAXMF, PF, NT_ROUTED>(A, J, sm.m);
+}
+
+template <int SF, int MAXMF>
+static hipError_t launch_mx_stages(const FfnArgs& a0, hipStream_t s) {
+  FfnArgs a = a0;
+  a.shared_slots = a.n_shared ? (a.T + MAXMF * 16 - 1) / (MAXMF * 16) : 0;
+  const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
+  const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
+  const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
+  const int64_t blocks = (int64_t)a.T * (a.d / 32);
+  x_to_mx_kernel<<<(unsigned)((blocks + 255) / 256), 256, 0, s>>>(
+      a.T, a.d, (const uint16_t*)a.hidden, a.xq, a.xsc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ffn_mx_kernel<SF, 1, MAXMF, LEAD_MX><<<slots * nb1, WAVES * 64, 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ffn_mx_kernel<SF, 2, MAXMF, LEAD_MX><<<slots * nb2, WAVES * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int SF>
+static hipError_t launch_mx_sf(const FfnArgs& a, hipStream_t s) {
+  if (a.T <= 16) return launch_mx_stages<SF, 1>(a, s);
+  if (a.T <= 32) return launch_mx_stages<SF, 2>(a, s);
+  return launch_mx_stages<SF, BM / 16>(a, s);
+}
+
+hipError_t launch_ffn_mx(const FfnArgs& a, hipStream_t s) {
+  const int sf = a.n_shared ? a.shared_fmt : MOE_BF16;
+  if (sf == MOE_BF16) return launch_mx_sf<MOE_BF16>(a, s);
+  if (sf == MOE_I8_ROW) return launch_mx_sf<MOE_I8_ROW>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

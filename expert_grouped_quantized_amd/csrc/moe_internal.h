@@ -36,6 +36,12 @@ constexpr int LEAD_WIDE = 2;
 constexpr int TILE_BYTES_BF16 = 64 * 64 * 2;        // 8192
 constexpr int TILE_BYTES_I4 = 64 * 64 / 2 + 64 * 2 * 2;  // 2048 codes + 256 scales
 constexpr int TILE_BYTES_I8 = 64 * 64;              // 4096 (row scales kept apart)
+// MXFP4 (scaled FP4 MFMA 16x16x128): a wave tile is 64 weight rows x 128 K,
+// 4096 bytes of e2m1 codes + 256 E8M0 scale bytes; its K loop keeps
+// LEAD_MX chunks in flight
+constexpr int KC_MX = 128;
+constexpr int TILE_BYTES_MX4 = 64 * 128 / 2 + 64 * 4;  // 4352
+constexpr int LEAD_MX = 2;
 
 // ---- route plan ----------------------------------------------------------
 constexpr int PLAN_CHUNK = 4096;   // assignments per block of the plan kernels
@@ -57,24 +63,28 @@ __host__ __device__ inline size_t tile_bytes(int fmt) {
   return fmt == MOE_BF16 ? TILE_BYTES_BF16
        : fmt == MOE_I4_G32 ? TILE_BYTES_I4
        : fmt == MOE_I8_ROW ? TILE_BYTES_I8
+       : fmt == MOE_MXFP4 ? TILE_BYTES_MX4
        : tile_bytes_ig32(ig32_bits(fmt));
 }
+// K of one wave tile
+__host__ __device__ constexpr int kc_of(int fmt) { return fmt == MOE_MXFP4 ? KC_MX : KC; }
 // K chunks each wave keeps in flight for a weight format: 4- and 2-bit codes
 // take LEAD_I4, the other tiles LEAD_WIDE (their registers)
 __host__ __device__ constexpr int lead_of(int fmt, int lead_i4) {
-  return (ig32_bits(fmt) == 4 || ig32_bits(fmt) == 2) ? lead_i4 : LEAD_WIDE;
+  return fmt == MOE_MXFP4 ? LEAD_MX
+       : (ig32_bits(fmt) == 4 || ig32_bits(fmt) == 2) ? lead_i4 : LEAD_WIDE;
 }
 
 // Bytes of the W1 (gate/up, [2F, d]) and W2 (down, [d, F]) sections of one
 // expert in the device blob.
 __host__ __device__ inline size_t w1_bytes(int fmt, size_t d, size_t F) {
   if (fmt == MOE_F32) return 2 * F * d * 4;
-  size_t tiles = (2 * F / 64) * (d / KC) * tile_bytes(fmt);  // 64-row wave tiles
+  size_t tiles = (2 * F / 64) * (d / kc_of(fmt)) * tile_bytes(fmt);  // 64-row wave tiles
   return tiles + (fmt == MOE_I8_ROW ? 2 * F * 2 : 0);
 }
 __host__ __device__ inline size_t w2_bytes(int fmt, size_t d, size_t F) {
   if (fmt == MOE_F32) return d * F * 4;
-  size_t tiles = (d / 64) * (F / KC) * tile_bytes(fmt);
+  size_t tiles = (d / 64) * (F / kc_of(fmt)) * tile_bytes(fmt);
   return tiles + (fmt == MOE_I8_ROW ? d * 2 : 0);
 }
 __host__ __device__ inline size_t expert_bytes(int fmt, size_t d, size_t F) {
@@ -90,9 +100,13 @@ struct WsLayout {
   size_t ntiles;       // int32 [1]             routed row tiles in the plan
   size_t tiles;        // int2  [routed_slots]  (expert, first row) per tile
   size_t h_routed;     // act-typed [T*k, F]    intermediate h, permuted rows
+                       //   (MXFP4 layers: e2m1 codes [T*k, F/2])
+  size_t h_scale;      // MXFP4 layers: E8M0 [T*k, F/32], the scales of h
   size_t h_shared;     // act-typed [T, Fs]     intermediate h of the shared expert
   size_t x16;          // fp16 [T, d]           activations scaled by 2^-xexp[t] (int4 path)
+                       //   (MXFP4 layers: e2m1 codes of x [T, d/2])
   size_t xexp;         // float [T]             2^xexp[t], the scale to undo
+                       //   (MXFP4 layers: E8M0 [T, d/32], the scales of x)
   size_t total;
 };
 
@@ -109,11 +123,13 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   L.counts = off;   off = align256(off + (size_t)L.n_chunks * D.n_experts * 4);
   L.ntiles = off;   off = align256(off + 4);
   L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 8);
-  L.h_routed = off; off = align256(off + (size_t)n * D.ffn * elem);
+  const bool mx = D.act == MOE_BF16 && D.expert_w == MOE_MXFP4;
+  L.h_routed = off; off = align256(off + (size_t)n * D.ffn * (mx ? 1 : 2 * elem) / 2);
+  L.h_scale = off;  off = align256(off + (mx ? (size_t)n * (D.ffn / 32) : 0));
   L.h_shared = off; off = align256(off + (D.n_shared ? (size_t)T * D.shared_ffn * elem : 0));
   const bool x16 = D.act == MOE_BF16 && ig32_bits(D.expert_w) != 0;
-  L.x16 = off;      off = align256(off + (x16 ? (size_t)T * D.d * 2 : 0));
-  L.xexp = off;     off = align256(off + (x16 ? (size_t)T * 4 : 0));
+  L.x16 = off;      off = align256(off + (x16 ? (size_t)T * D.d * 2 : mx ? (size_t)T * D.d / 2 : 0));
+  L.xexp = off;     off = align256(off + (x16 ? (size_t)T * 4 : mx ? (size_t)T * (D.d / 32) : 0));
   L.total = off;
   return L;
 }
@@ -144,6 +160,11 @@ struct FfnArgs {
   void* h_shared;
   uint16_t* x16;    // fp16 activations of the int4 path (workspace)
   float* xscale;    // per-token power of two undone in the gate/up epilogue
+  // MXFP4 layers (workspace): e2m1 codes and E8M0 scales of x and of h
+  uint8_t* xq;
+  uint8_t* xsc;
+  uint8_t* hq;
+  uint8_t* hsc;
   float* out_assign;
   float* shared_out;
 };
@@ -151,6 +172,8 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
 // routed weights in the 2, 3, 5, 6, 7 or 8-bit group-32 formats
 hipError_t launch_ffn_lowbit(const FfnArgs& a, hipStream_t s);
+// MXFP4 W4A4 routed experts
+hipError_t launch_ffn_mx(const FfnArgs& a, hipStream_t s);
 // x -> fp16 copy and per-token scale (int4 layers)
 hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,

@@ -18,6 +18,10 @@
  *     chapter 17, section 17.2: expert packs coded at other bit widths, MoE
  *     kernels that take 2 to 6 and 8 bits (here 2, 3, 5, 6, 7 and 8-bit
  *     group-32 codes beside int4).
+ *   - "anvil-serving" benchmark dossier, Qwen3.8-Flash-Next entry, section
+ *     "Quantization boundary": W4A4 (4-bit weights and activations) on the
+ *     routed experts only, the shared expert kept 16-bit.  Here in the OCP
+ *     Microscaling FP4 format that CDNA4's scaled MFMA takes (MOE_MXFP4).
  *
  * Conventions for every call below:
  *   - Ownership: the caller allocates and frees every buffer.  The library
@@ -51,6 +55,12 @@
  *     scale per 32 consecutive elements along K, scales [rows, K/32].  Weight
  *     value = code * scale.  The device blob stores them at b bits per weight
  *     (plus the scales).
+ *   MOE_MXFP4: OCP MX FP4 (e2m1) codes, byte j of a row holds element 2j in its
+ *     low nibble, [rows, K/2]; one E8M0 scale byte per 32 consecutive elements
+ *     along K, scales [rows, K/32] (uint8).  Weight value = e2m1(code) *
+ *     2^(scale - 127); e2m1 is sign bit 3, exponent bits 2..1 (bias 1),
+ *     mantissa bit 0, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  A scale byte of
+ *     255 (NaN) is rejected by the packer.
  * The device blob written by moe_pack_experts is a private, tile-ordered
  * layout; its only contract is moe_pack_experts / moe_unpack_experts.
  */
@@ -84,7 +94,8 @@ typedef enum moe_dtype {
   MOE_I5_G32 = 6,
   MOE_I6_G32 = 7,
   MOE_I7_G32 = 8,
-  MOE_I8_G32 = 9
+  MOE_I8_G32 = 9,
+  MOE_MXFP4 = 10  /* OCP MX FP4: e2m1 codes + E8M0 scale per 32 along K (W4A4) */
 } moe_dtype;
 
 typedef enum moe_blob_kind {
@@ -95,11 +106,12 @@ typedef enum moe_blob_kind {
 /* Shape and storage of one MoE layer.
  * Supported combinations:
  *   act MOE_F32 : expert_w MOE_F32, shared_w MOE_F32 (router fp32, y fp32)
- *   act MOE_BF16: expert_w MOE_BF16, MOE_I4_G32 or MOE_I{2,3,5,6,7,8}_G32,
- *                 shared_w MOE_BF16 or MOE_I8_ROW  (router bf16, y bf16)
+ *   act MOE_BF16: expert_w MOE_BF16, MOE_I4_G32, MOE_I{2,3,5,6,7,8}_G32 or
+ *                 MOE_MXFP4, shared_w MOE_BF16 or MOE_I8_ROW  (router bf16,
+ *                 y bf16)
  * Sizes: 1 <= n_experts <= 1024; n_shared 0 or 1.  For act MOE_BF16:
- * d % 256 == 0, ffn % 128 == 0 (% 256 with 2- or 4-bit routed weights),
- * shared_ffn % 128 == 0.  For act MOE_F32:
+ * d % 256 == 0, ffn % 128 == 0 (% 256 with 2- or 4-bit or MXFP4 routed
+ * weights), shared_ffn % 128 == 0.  For act MOE_F32:
  * d, ffn, shared_ffn multiples of 64.  d, ffn, shared_ffn <= 16384.         */
 typedef struct moe_desc {
   int32_t d;          /* hidden width                                       */
@@ -133,7 +145,8 @@ moe_status moe_blob_bytes(const moe_desc* desc, int32_t kind, size_t* bytes);
  * (>= moe_blob_bytes).  The caller copies it to device memory.  For ROUTED the
  * inputs hold n_experts experts stacked; for SHARED one expert.
  * MOE_I4_G32 codes must lie in [-7, 7] (symmetric); an 8 (-8) code returns
- * MOE_EINVAL, as does a b-bit code outside [-(2^(b-1) - 1), 2^(b-1) - 1].
+ * MOE_EINVAL, as does a b-bit code outside [-(2^(b-1) - 1), 2^(b-1) - 1] and
+ * an MXFP4 scale byte of 255.
  * Host only.                                                                */
 moe_status moe_pack_experts(const moe_desc* desc, int32_t kind, const void* gate,
                             const void* gate_scales, const void* up, const void* up_scales,
@@ -209,7 +222,16 @@ moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const int32_t
  * bf16(code * scale) in the down product; int8 codes enter exactly, their row
  * scale applied to the
  * fp32 accumulator.  h is rounded to bf16 (nearest even); the outputs stay
- * fp32.  The fp32 path computes and stores in fp32 throughout.              */
+ * fp32.  The fp32 path computes and stores in fp32 throughout.
+ * MOE_MXFP4 routed experts run W4A4 on the scaled FP4 MFMA: each token row of
+ * hidden is quantized to MXFP4 block by block of 32 (OCP MX rule: shared
+ * exponent E = floor(log2 max|v|) - 2, clamped to [-127, 127], -127 for an
+ * all-zero block; element = nearest e2m1 value of v / 2^E, ties to even,
+ * saturated at +-6), the gate/up products and h = w * silu(g) * u are
+ * computed in fp32, h is quantized the same way per row and 32 columns
+ * (straight from fp32), and the down product runs on those codes; fp32
+ * accumulation throughout.  The shared expert of such a layer runs on the
+ * unquantized bf16 hidden rows (bf16 MFMA).                                */
 moe_status moe_grouped_ffn(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
                            const void* routed_blob, const void* shared_blob, float* out_assign,

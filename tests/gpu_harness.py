@@ -10,7 +10,7 @@ import workloads as W
 from expert_grouped_quantized_amd.layer import MoELayer, blobs_from_inputs
 
 ORC_FMT = {W.F32: oracle.F32, W.BF16: oracle.BF16, W.I4G32: oracle.I4G32, W.I8ROW: oracle.I8ROW,
-           **{name: oracle.FMT_NAMES[name] for name in W.IG32.values()}}
+           W.MXFP4: oracle.MXFP4, **{name: oracle.FMT_NAMES[name] for name in W.IG32.values()}}
 
 
 def desc_of(cfg: W.LayerConfig):
@@ -109,8 +109,54 @@ def check_plan(cfg, out):
     assert np.array_equal(out["inv_perm"], inv), "inv_perm differs"
 
 
+def mx_error_constants(cfg):
+    """fp32 error model of the W4A4 path: gamma of the gate/up and of the down
+    dot products (one rounding per 32-element block of the MFMA chain,
+    doubled, plus eight), eta of the elementwise steps that make h."""
+    return (cfg.d / 16 + 8) * 2.0 ** -24, (cfg.F / 16 + 8) * 2.0 ** -24, 2.0 ** -16
+
+
+def check_values_mx(cfg, inputs, out, w_o, tokens=None):
+    """MXFP4 W4A4 routed experts.  x's codes are decisions on exact inputs and
+    must match; h's codes are decisions on a computed h, so where h lies within
+    its fp32 error of a decision boundary either code is correct: the oracle
+    returns, per output element, mag = sum |Wd hq| and the largest change such
+    a decision can make (slack).  Bound on out_assign, per element:
+    |gpu - ref| <= gamma_F (mag + slack) + slack.  y: rel-L2 <= 5e-3 and
+    max-abs <= 2e-2 max|ref| + the slack of its k assignments."""
+    T = out["ids"].shape[0]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    g_gu, g_dn, eta = mx_error_constants(cfg)
+    y_ref, oa_ref, so_ref, slack, mag = oracle.moe_experts_mx(
+        spec_of(cfg), inputs, out["ids"][tok], w_o[tok], g_gu, eta, tokens=tok)
+    flat = (tok[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
+    gpu_oa = out["out_assign"][out["inv_perm"][flat]].astype(np.float64)
+    err = np.abs(gpu_oa - oa_ref)
+    tight = g_dn * (mag + slack)
+    bound = tight + slack
+    bad = err > bound
+    assert not bad.any(), (f"out_assign: {int(bad.sum())} elements beyond the W4A4 bound, worst "
+                           f"err {err[bad].max():.3e} vs bound {bound[bad][np.argmax(err[bad])]:.3e}")
+    r_oa = rel_l2(gpu_oa, oa_ref)
+    assert r_oa <= 5e-3, f"out_assign: rel-L2 {r_oa:.3e} > 5e-3"
+    y_gpu = np.asarray(out["y"][tok], np.float64)
+    r_y = rel_l2(y_gpu, y_ref)
+    assert r_y <= 5e-3, f"y: rel-L2 {r_y:.3e} > 5e-3"
+    lim = 2e-2 * np.max(np.abs(y_ref)) + slack.reshape(len(tok), cfg.k, cfg.d).sum(axis=1)
+    over = np.abs(y_gpu - y_ref) > lim
+    assert not over.any(), f"y: {int(over.sum())} elements beyond 2e-2 max|ref| + slack"
+    r_so = None
+    if cfg.n_shared:
+        r_so = assert_close(out["shared_out"][tok], so_ref, False, "shared_out")
+    return dict(y=r_y, out_assign=r_oa, shared_out=r_so,
+                rows_with_slack=int((slack > 0).any(axis=1).sum()),
+                elements_using_slack=int((err > tight).sum()))
+
+
 def check_values(cfg, inputs, out, w_o, tokens=None):
     """y, out_assign and shared_out of the chosen tokens against the oracle."""
+    if cfg.expert == W.MXFP4:
+        return check_values_mx(cfg, inputs, out, w_o, tokens)
     T = out["ids"].shape[0]
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     fp32 = cfg.act == W.F32

@@ -148,7 +148,7 @@ def _rand_expert(fmt, rows, K, n, rng):
 @pytest.mark.parametrize("act,fmt,kind", [("bf16", "bf16", 0), ("bf16", "i4g32", 0),
                                           ("bf16", "i8row", 1), ("bf16", "bf16", 1),
                                           ("f32", "f32", 0), ("f32", "f32", 1)]
-                         + [("bf16", f, 0) for f in W.IG32.values()])
+                         + [("bf16", f, 0) for f in W.IG32.values()] + [("bf16", "mxfp4", 0)])
 def test_pack_unpack_roundtrip(act, fmt, kind):
     rng = np.random.default_rng(hash((act, fmt, kind)) % 2**32)
     d, F, E = (256, 256, 3) if act == "bf16" else (128, 64, 2)
@@ -220,3 +220,26 @@ def test_bbit_formats_only_for_routed_weights_and_2bit_needs_ffn_256():
         M.moe_blob_bytes(M.make_desc(256, 4, 384, 0, 0, act="bf16", expert_w="i2g32"), 0)
     assert ei.value.status == M.MOE_EUNSUPPORTED and "256" in str(ei.value)
     M.moe_blob_bytes(M.make_desc(256, 4, 384, 0, 0, act="bf16", expert_w="i3g32"), 0)
+
+
+def test_mxfp4_blob_bytes_rejections_and_width():
+    """MXFP4: 4 bits a weight plus one E8M0 byte per 32; routed weights only;
+    d and ffn multiples of 256; a NaN scale (255) is rejected."""
+    per_w = 3 * 1024 * 2560
+    assert M.moe_blob_bytes(_desc(expert_w="mxfp4"), M.MOE_BLOB_ROUTED) == 512 * per_w * 17 // 32
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_blob_bytes(_desc(shared_w="mxfp4"), 0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_blob_bytes(M.make_desc(256, 4, 384, 0, 0, act="bf16", expert_w="mxfp4"), 0)
+    assert ei.value.status == M.MOE_EUNSUPPORTED and "256" in str(ei.value)
+    desc = M.make_desc(256, 2, 256, 0, 0, act="bf16", expert_w="mxfp4")
+    q = np.zeros((2, 256, 128), np.uint8)
+    s = np.full((2, 256, 8), 127, np.uint8)
+    blob = np.empty(M.moe_blob_bytes(desc, 0), np.uint8)
+    M.moe_pack_experts(desc, 0, q, s, q, s, q, s, blob)
+    bad = s.copy()
+    bad[1, 17, 3] = 255
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_pack_experts(desc, 0, q, s, q, s, q, bad, blob)
+    assert ei.value.status == M.MOE_EINVAL and "expert 1" in str(ei.value) and "255" in str(ei.value)

@@ -77,6 +77,12 @@ def _small_cfg(name, idx, **kw):
     _small_cfg("i6_T20", 23, expert=W.IG32[6], T=20),
     _small_cfg("i7_T5", 24, expert=W.IG32[7], T=5),
     _small_cfg("i8g_T77", 25, expert=W.IG32[8], T=77, F=128),
+    # MXFP4 W4A4 routed experts (scaled FP4 MFMA), every tile size
+    _small_cfg("mx_T300", 26, expert=W.MXFP4),
+    _small_cfg("mx_bf16shared_d512", 27, expert=W.MXFP4, shared=W.BF16, T=129, d=512, F=512),
+    _small_cfg("mx_T20", 28, expert=W.MXFP4, T=20),
+    _small_cfg("mx_T5_noshared", 29, expert=W.MXFP4, T=5, n_shared=0, Fs=0),
+    _small_cfg("mx_E1_k1", 30, expert=W.MXFP4, E=1, k=1, n_shared=0, Fs=0, T=200),
 ], ids=lambda c: c.name)
 def test_small_shapes_full(cfg):
     inp = W.generate(cfg)
@@ -157,12 +163,37 @@ def test_activation_rows_over_a_wide_range():
     _say("[ok] range", f"worst row rel-L2 {max(rel_l2(out['y'][t], y_ref[t]) for t in range(cfg.T) if t != 7):.2e}")
 
 
-@pytest.mark.parametrize("T", [16, 40])
-def test_graph_replay_matches_eager(T):
+def test_mxfp4_activation_ties_and_row_scales():
+    """W4A4: x rows made of exact ties of the e2m1 rounding (each block's
+    maximum 1.9375 sets the scale 2^-2; the other elements sit at 0.25 x
+    {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 7}, so every tie and the clamp at 6
+    occur), each row scaled by its own power of two, one row zero.  A tie
+    broken the other way would move g and u far beyond the tight W4A4 bound."""
+    cfg = _small_cfg("mx_ties", 31, expert=W.MXFP4, T=64)
+    inp = W.generate(cfg)
+    rng = np.random.default_rng(31)
+    ties = 0.25 * np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0])
+    x = rng.choice(ties, size=(cfg.T, cfg.d)) * rng.choice([-1.0, 1.0], size=(cfg.T, cfg.d))
+    x[:, ::32] = 1.9375 * rng.choice([-1.0, 1.0], size=(cfg.T, cfg.d // 32))
+    x *= np.exp2(rng.integers(-30, 31, size=cfg.T))[:, None]
+    x[9] = 0.0
+    inp["x"] = W.to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(inp["x"]).astype(np.float64), x)  # exact in bf16
+    g = GpuLayer(cfg, inp)
+    out = g.run(inp["x"])
+    ids_o, w_o = check_route(cfg, inp, out)
+    check_plan(cfg, out)
+    r = check_values(cfg, inp, out, w_o)
+    assert not out["y"][9].any(), "a zero row gives exactly zero"
+    _say("[ok] mx_ties", r)
+
+
+@pytest.mark.parametrize("T,expert", [(16, W.I4G32), (40, W.I4G32), (16, W.MXFP4)])
+def test_graph_replay_matches_eager(T, expert):
     """The four calls captured as one HIP graph: every replay, with eager calls
     on another input between the replays, equals the eager result bit for bit
     (no call records a memset; every buffer is the caller's)."""
-    cfg = _small_cfg(f"graph{T}", 14, T=T)
+    cfg = _small_cfg(f"graph{T}", 14, T=T, expert=expert)
     inp = W.generate(cfg)
     g = GpuLayer(cfg, inp)
     x_a = inp["x"]
@@ -186,7 +217,7 @@ def test_graph_replay_matches_eager(T):
 
 
 @pytest.mark.parametrize("expert,shared", [(W.I4G32, W.I8ROW), (W.BF16, W.BF16),
-                                           (W.IG32[5], W.I8ROW)])
+                                           (W.IG32[5], W.I8ROW), (W.MXFP4, W.I8ROW)])
 def test_rows_do_not_depend_on_the_batch(expert, shared):
     """A token's logits and output bits are the same whichever kernels its
     call size selects: 300 tokens (large-T router, 96-row tiles), 40 (small-T
@@ -300,6 +331,45 @@ def test_int4_decode_full(T):
     check_plan(cfg, out)
     r = check_values(cfg, inp, out, w_o)
     _say(f"[ok] int4_decode T={T}", r, "active experts", int((np.diff(out['offsets']) > 0).sum()))
+
+
+def _mx_variant(name, T=None):
+    """The named workload with MXFP4 W4A4 routed experts (same draws)."""
+    from dataclasses import replace
+    key = (name + "/mxfp4", T)
+    if key not in _CACHE:
+        cfg = replace(W.CONFIGS[name], name=name + "_mxfp4", expert=W.MXFP4)
+        _say(f"[gen] {cfg.name} T={T or cfg.T}")
+        inputs = W.generate(cfg, T=T)
+        _CACHE.clear()
+        _CACHE[key] = (cfg, inputs, GpuLayer(cfg, inputs))
+    return _CACHE[key]
+
+
+def test_mxfp4_T4096_sampled():
+    cfg, inp, g = _mx_variant("int4_T4096")
+    _say("[run] mxfp4 T=4096")
+    out = g.run(inp["x"])
+    tok = _sample(cfg.T, 24, 6)
+    ids_o, w_o = check_route(cfg, inp, out, tokens=tok)
+    check_plan(cfg, out)
+    r = check_values(cfg, inp, out, w_o, tokens=tok)
+    _say("[ok] mxfp4 T=4096", r)
+    out2 = g.run(inp["x"])
+    for key in ("out_assign", "shared_out", "y_bits"):
+        assert np.array_equal(out[key], out2[key]), f"{key} not bitwise repeatable"
+
+
+@pytest.mark.parametrize("T", [16, 32])
+def test_mxfp4_decode_full(T):
+    cfg, inp, g = _mx_variant("int4_decode", T=T)
+    cfg = cfg.with_T(T)
+    _say(f"[run] mxfp4 decode T={T}")
+    out = g.run(inp["x"])
+    ids_o, w_o = check_route(cfg, inp, out)
+    check_plan(cfg, out)
+    r = check_values(cfg, inp, out, w_o)
+    _say(f"[ok] mxfp4 decode T={T}", r)
 
 
 def test_zipf_T16384_sampled():
