@@ -137,20 +137,23 @@ struct SmemMx {
 };
 
 // Stage-1 epilogue: h = w * silu(g) * u of the wave's 32 h columns, quantized
-// to MXFP4 per row (the 32 columns are one block), codes into hq (row-major,
-// F/2 bytes a row) and scales into hsc (F/32 bytes a row).  Row
-// i*16 + 4*(lane/16) + r of the tile holds, in lane l, column 16 f + l % 16
-// for f = 0, 1 (gate fragments f, up fragments f + 2).  The row maximum runs
-// over the 16 lanes of a DPP row; lanes l and l^1 then trade their codes and
-// each writes whole bytes (two columns) of two rows.
+// to MXFP4 per row (the 32 columns are one block).  Row i*16 + 4*(lane/16) + r
+// of the tile holds, in lane l, column 16 f + l % 16 for f = 0, 1 (gate
+// fragments f, up fragments f + 2).  The row maximum runs over the 16 lanes of
+// a DPP row; lanes l and l^1 then trade their codes so each lane holds whole
+// bytes (two columns) of two rows.  The block's codes (64 bytes a row: 16 per
+// wave) and scales (4 bytes a row) are gathered in LDS (`hl`, `sl`, free after
+// the K loop) and leave as one 16-byte store per row piece and one 4-byte
+// store per row: hq is row-major (F/2 bytes a row), hsc F/32 bytes a row.
 template <int NMF, typename RowW>
-__device__ __forceinline__ void store_h_mx(const FfnArgs& A, int start, int cnt, int run,
-                                           const f32x4_t (&acc)[NMF][4], RowW wrow) {
-  const int lane = threadIdx.x & 63, c = lane & 15, quad = 4 * (lane >> 4);
+__device__ __forceinline__ void store_h_mx(const FfnArgs& A, int start, int cnt, int nb,
+                                           const f32x4_t (&acc)[NMF][4], RowW wrow, uint8_t* hl,
+                                           uint8_t* sl) {
+  constexpr int ROWS = NMF * 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, quad = 4 * (lane >> 4);
   const bool odd = lane & 1;
-  const size_t qs = (size_t)A.F / 2, ss = (size_t)A.F / 32;
-  uint8_t* hq = A.hq + (size_t)start * qs + run * 16 + (c >> 1);
-  uint8_t* hs = A.hsc + (size_t)start * ss + run;
+  __syncthreads();  // every wave is done reading the staging buffers
 #pragma unroll
   for (int i = 0; i < NMF; i++) {
     float h0[4], h1[4];
@@ -181,22 +184,29 @@ __device__ __forceinline__ void store_h_mx(const FfnArgs& A, int start, int cnt,
     const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, 0xB1, 0xF, 0xF, false);
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      const int r = odd ? 2 + q : q;  // the even lane writes rows 0, 1, the odd lane 2, 3
+      const int r = odd ? 2 + q : q;  // the even lane takes rows 0, 1, the odd lane 2, 3
       const int row = i * 16 + quad + r;
 #pragma unroll
       for (int f = 0; f < 2; f++) {
         const int n = 4 * (4 * f + r);
         const uint32_t mine = (code >> n) & 15u, oth = (other >> n) & 15u;
-        const uint32_t byte = odd ? (oth | (mine << 4)) : (mine | (oth << 4));
-        if (row < cnt) hq[(size_t)row * qs + 8 * f] = (uint8_t)byte;
+        hl[row * 64 + wave * 16 + 8 * f + (c >> 1)] =
+            (uint8_t)(odd ? (oth | (mine << 4)) : (mine | (oth << 4)));
       }
     }
-    if (c < 4) {
-      const int row = i * 16 + quad + c;
-      const uint32_t e = c == 0 ? eb[0] : c == 1 ? eb[1] : c == 2 ? eb[2] : eb[3];
-      if (row < cnt) hs[(size_t)row * ss] = (uint8_t)e;
-    }
+    if (c < 4) sl[(i * 16 + quad + c) * 4 + wave] = (uint8_t)(c == 0 ? eb[0] : c == 1 ? eb[1] : c == 2 ? eb[2] : eb[3]);
   }
+  __syncthreads();
+  const size_t qs = (size_t)A.F / 2, ss = (size_t)A.F / 32;
+#pragma unroll
+  for (int q = tid; q < ROWS * 4; q += WAVES * 64) {
+    const int row = q >> 2, part = q & 3;
+    if (row < cnt)
+      *(u32x4_t*)(A.hq + (size_t)(start + row) * qs + nb * 64 + part * 16) =
+          *(const u32x4_t*)(hl + row * 64 + part * 16);
+  }
+  if (tid < ROWS && tid < cnt)
+    *(uint32_t*)(A.hsc + (size_t)(start + tid) * ss + nb * 4) = *(const uint32_t*)(sl + tid * 4);
 }
 
 // One routed (row tile, column block) of an MXFP4 layer.
@@ -207,7 +217,7 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   constexpr int PIECES = ROWS * 4;  // 16-byte code pieces of one chunk
   constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
   static_assert(PPT <= 2, "code staging holds at most 2 pieces per thread");
-  static_assert(PF == 2 || PF == 4, "load lead must be 2 or 4 chunks");
+  static_assert(PF == 2, "the scale pairs below assume a lead of two chunks");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = STAGE == 1 ? A.d : A.F;
   const int nk = K / KC_MX;
@@ -262,18 +272,21 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
 #pragma unroll
     for (int f = 0; f < 4; f++) acc[i][f] = f32x4_t{0, 0, 0, 0};
 
+  // Ring slot p holds chunk kc with kc % 2 == p.  The scales of an even chunk
+  // and the next one arrive together in `apair` (one 8-byte load per row
+  // every two chunks; K/32 is a multiple of 8, so the pair is aligned).
   u32x4_t areg[PF][PPT];
-  uint32_t asreg[PF];
+  uint2 apair;
   auto load_a = [&](int kc, int p) {
 #pragma unroll
     for (int j = 0; j < PPT; j++) areg[p][j] = *(const u32x4_t*)(aq[j] + kc * (KC_MX / 2));
-    asreg[p] = *(const uint32_t*)(as + kc * 4);
+    if (p == 0) apair = *(const uint2*)(as + kc * 4);
   };
-  auto store_a = [&](int buf, int p) {
+  auto store_a = [&](int buf, int p, uint32_t sc) {
 #pragma unroll
     for (int j = 0; j < PPT; j++) *(u32x4_t*)(sm.a[buf] + aq_lds[j]) = areg[p][j];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) sm.s[buf][kb * 128 + s_lds] = (uint8_t)(asreg[p] >> (8 * kb));
+    for (int kb = 0; kb < 4; kb++) sm.s[buf][kb * 128 + s_lds] = (uint8_t)(sc >> (8 * kb));
   };
   const int am = lane & 15, akb = lane >> 4;
   auto compute = [&](int buf, const WTileMx& w) {
@@ -298,9 +311,9 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
     });
   };
 
-  // The peeled pipeline of ffn_kernels.h's tile_body: step kc issues the
-  // activation and weight loads of chunk kc + PF in the order they are
-  // waited for; nk is a multiple of PF (the ABI's width checks).
+  // The peeled pipeline of ffn_kernels.h's tile_body with a lead of two
+  // chunks: step kc issues the activation and weight loads of chunk kc + 2 in
+  // the order they are waited for; nk is even (the ABI's width checks).
   WTileMx ring[PF];
 #pragma unroll
   for (int p = 0; p < PF; p++) {
@@ -308,33 +321,38 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
     ring[p].template load<NT>(wnext, lane);
     wnext += TILE_BYTES_MX4;
   }
-  store_a(0, 0);
+  store_a(0, 0, apair.x);
   __syncthreads();
   for (int kc0 = 0; kc0 < nk - PF; kc0 += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; p++) {
-      load_a(kc0 + p + PF, p);  // set p held chunk kc0 + p, already in LDS
-      compute(p & 1, ring[p]);
-      ring[p].template load<NT>(wnext, lane);
-      wnext += TILE_BYTES_MX4;
-      store_a((p + 1) & 1, (p + 1) % PF);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // step 0: chunk kc0 from LDS; loads of chunk kc0 + 2 (and the scale pair
+    // of kc0 + 2, kc0 + 3); stages chunk kc0 + 1, whose scale is the odd half
+    // of the pair being replaced
+    const uint32_t s_odd = apair.y;
+    load_a(kc0 + 2, 0);
+    compute(0, ring[0]);
+    ring[0].template load<NT>(wnext, lane);
+    wnext += TILE_BYTES_MX4;
+    store_a(1, 1, s_odd);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1: chunk kc0 + 1; loads of chunk kc0 + 3; stages chunk kc0 + 2
+    load_a(kc0 + 3, 1);
+    compute(1, ring[1]);
+    ring[1].template load<NT>(wnext, lane);
+    wnext += TILE_BYTES_MX4;
+    store_a(0, 0, apair.x);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
-#pragma unroll
-  for (int p = 0; p < PF; p++) {
-    compute(p & 1, ring[p]);
-    if (p + 1 < PF) {
-      store_a((p + 1) & 1, p + 1);
-      __syncthreads();
-    }
-  }
+  compute(0, ring[0]);  // the last two chunks: nothing more to load
+  store_a(1, 1, apair.y);
+  __syncthreads();
+  compute(1, ring[1]);
 
   const int quad = 4 * (lane >> 4);
   auto wrow = [&](int i, int r) { return sm.wrow[i * 16 + quad + r]; };
   if constexpr (STAGE == 1) {
-    store_h_mx<NMF>(A, J.start, J.cnt, run, acc, wrow);
+    store_h_mx<NMF>(A, J.start, J.cnt, J.nb, acc, wrow, sm.a[0], sm.s[0]);
   } else {
     store_wave_tile<MOE_MXFP4, 2, NMF, false>(A, false, J.start, J.cnt, run, A.F, sect, acc, wrow,
                                                [](int, int) { return 1.0f; });
