@@ -217,6 +217,7 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   constexpr int PIECES = ROWS * 4;  // 16-byte code pieces of one chunk
   constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
   static_assert(PPT <= 2, "code staging holds at most 2 pieces per thread");
+  static_assert(MAXMF > 2 || PPT == 1, "small tiles stage one piece per thread");
   static_assert(PF == 2, "the scale pairs below assume a lead of two chunks");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = STAGE == 1 ? A.d : A.F;
@@ -277,16 +278,26 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   // every two chunks; K/32 is a multiple of 8, so the pair is aligned).
   u32x4_t areg[PF][PPT];
   uint2 apair;
+  // Small tiles have fewer pieces than threads: only the threads that own a
+  // distinct piece (whole waves) load and stage it.  Large tiles let every
+  // thread load (some pieces twice, same bytes to the same place): measured,
+  // the predicated form is much slower there.
+  constexpr bool PRED = MAXMF <= 2;
+  const bool own0 = !PRED || tid < PIECES, own_s = !PRED || tid < ROWS;
   auto load_a = [&](int kc, int p) {
 #pragma unroll
-    for (int j = 0; j < PPT; j++) areg[p][j] = *(const u32x4_t*)(aq[j] + kc * (KC_MX / 2));
-    if (p == 0) apair = *(const uint2*)(as + kc * 4);
+    for (int j = 0; j < PPT; j++)
+      if (own0) areg[p][j] = *(const u32x4_t*)(aq[j] + kc * (KC_MX / 2));
+    if (p == 0 && own_s) apair = *(const uint2*)(as + kc * 4);
   };
   auto store_a = [&](int buf, int p, uint32_t sc) {
 #pragma unroll
-    for (int j = 0; j < PPT; j++) *(u32x4_t*)(sm.a[buf] + aq_lds[j]) = areg[p][j];
+    for (int j = 0; j < PPT; j++)
+      if (own0) *(u32x4_t*)(sm.a[buf] + aq_lds[j]) = areg[p][j];
+    if (own_s) {
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) sm.s[buf][kb * 128 + s_lds] = (uint8_t)(sc >> (8 * kb));
+      for (int kb = 0; kb < 4; kb++) sm.s[buf][kb * 128 + s_lds] = (uint8_t)(sc >> (8 * kb));
+    }
   };
   const int am = lane & 15, akb = lane >> 4;
   auto compute = [&](int buf, const WTileMx& w) {
