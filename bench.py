@@ -215,21 +215,33 @@ def cpu_baseline(cfg, inp: dict, T: int, n_tok: int):
                       f"(fp64 router, top-k, per-expert SwiGLU, shared expert, sum); {dt:.1f} s"}
 
 
+GEMM_SOURCES = ("ffn.hip", "ffn_kernels.h", "wave_tile.h", "moe_internal.h", "device_common.h")
+MX_SOURCES = ("ffn_mx.hip", "ffn_kernels.h", "wave_tile.h", "moe_internal.h", "device_common.h")
+
+
+def sources_sha(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "expert_grouped_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def counted_traffic(workload: str):
     """HBM bytes per moe_grouped_ffn launch from the committed rocprofv3 counter
     runs (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE, each scaled by
-    what it reads for a 1 GiB copy), or None once the GEMM kernel sources have
-    changed since those counters were taken."""
-    import hashlib
+    what it reads for a 1 GiB copy), or None once the sources of the kernels
+    that launch runs have changed since those counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in ("ffn.hip", "ffn_kernels.h", "wave_tile.h", "moe_internal.h", "device_common.h"):
-        with open(os.path.join(ROOT, "expert_grouped_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if rec.get("src_sha256") != h.hexdigest() or workload not in rec:
+    if workload not in rec:
+        return None
+    files = MX_SOURCES if workload.startswith("mxfp4") else GEMM_SOURCES
+    key = "mx_src_sha256" if workload.startswith("mxfp4") else "src_sha256"
+    if rec.get(key) != sources_sha(files):
         return None
     return rec[workload]["grouped_ffn_bytes_per_launch"]
 
@@ -369,6 +381,12 @@ def run_mxfp4(args, torch, W):
                ffn_gbs=A["ffn_bytes"] / ffn_s / 1e9,
                ffn_hbm_frac=A["ffn_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS)
     out = {"prefill": pre}
+    out["roofline"] = {
+        "bound": "hbm", "kernel": "moe_grouped_ffn (x -> MXFP4, FP4 gate/up + h -> MXFP4, FP4 down)",
+        "achieved": round(pre["ffn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(pre["ffn_hbm_frac"], 4), "traffic": counted_traffic("mxfp4_prefill"),
+        "algorithmic_bytes_per_launch": A["ffn_bytes"], "avg_launch_ms": round(per[2], 4),
+        "fp4_mfma_frac": round(pre["ffn_fp4_mfma_frac"], 4)}
     for T in (16, 32):
         D = _View(S, T)
         D.step(0)
@@ -384,6 +402,12 @@ def run_mxfp4(args, torch, W):
                                     combine=dper[3]),
                        ffn_weight_gbs=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9,
                        ffn_weight_hbm_frac=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            out["decode_roofline"] = {
+                "bound": "hbm", "kernel": "moe_grouped_ffn at T=16 (weight streams)",
+                "achieved": round(rec["ffn_weight_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(rec["ffn_weight_hbm_frac"], 4),
+                "traffic": counted_traffic("mxfp4_decode"),
+                "algorithmic_bytes_per_launch": DA["weight_bytes"], "avg_launch_ms": round(dper[2], 4)}
         g_ms, g_ev = time_graph(D, args.decode_steps)
         rec["graph"] = dict(ms_per_step=g_ms, event_ms_per_step=g_ev, tokens_per_s=T / (g_ms * 1e-3),
                             layer_hbm_frac=DA["layer_bytes"] / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
