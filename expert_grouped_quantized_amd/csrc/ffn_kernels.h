@@ -221,6 +221,26 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
   tile_body<FMT, STAGE, MAXMF, PF_MAX, F16, NT>(A, J, sm, C);
 }
 
+// A routed tile of a 96-row kernel with fewer rows runs a body with fewer row
+// fragments (2, 4 or 5): the MFMAs of padding fragments are never issued, and
+// the branch is taken once per tile, outside the MFMA stream.  Every body
+// computes a row with the same MFMA chain and epilogue (row invariance).
+// Measured at T=4096: grouped FFN -3.6% (about half the tiles hold <= 80
+// rows; experts spilling past 96 rows leave small second tiles).
+template <int RF, int STAGE, int MAXMF, int PF, bool F16, bool NT>
+__device__ __forceinline__ void run_routed_tile(const FfnArgs& A, const TileJob& J,
+                                                Smem<MAXMF>& sm) {
+  if constexpr (MAXMF == 6) {
+    if (J.cnt <= 32)
+      return run_tile<RF, STAGE, 2, PF, F16, NT>(A, J, *reinterpret_cast<Smem<2>*>(&sm));
+    if (J.cnt <= 64)
+      return run_tile<RF, STAGE, 4, PF, F16, NT>(A, J, *reinterpret_cast<Smem<4>*>(&sm));
+    if (J.cnt <= 80)
+      return run_tile<RF, STAGE, 5, PF, F16, NT>(A, J, *reinterpret_cast<Smem<5>*>(&sm));
+  }
+  run_tile<RF, STAGE, MAXMF, PF, F16, NT>(A, J, sm);
+}
+
 // Grid: slot-major with the column block fastest *within an XCD*: block b runs
 // on XCD b % 8; slot = (b / (8*NB)) * 8 + b % 8, nb = (b / 8) % NB.  So all
 // column blocks of one row tile share an XCD (and its L2 copy of the gathered
@@ -268,7 +288,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   if (J.shared)
     run_tile<SF, STAGE, MAXMF, PF, STAGE == 1 && X16 && SF == MOE_I8_ROW, NT_SHARED>(A, J, sm);
   else
-    run_tile<RF, STAGE, MAXMF, PF, STAGE == 1 && X16, NT_ROUTED>(A, J, sm);
+    run_routed_tile<RF, STAGE, MAXMF, PF, STAGE == 1 && X16, NT_ROUTED>(A, J, sm);
 }
 
 // Row tiles come from the route plan (at most BM = 96 rows each).  A call

@@ -370,6 +370,22 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   }
 }
 
+// Routed tiles of a 96-row kernel with fewer rows run a body with fewer row
+// fragments (as run_routed_tile in ffn_kernels.h; measured -1% at T=4096).
+template <int STAGE, int MAXMF, int PF, bool NT>
+__device__ __forceinline__ void run_routed_tile_mx(const FfnArgs& A, const TileJob& J,
+                                                   SmemMx<MAXMF>& sm) {
+  if constexpr (MAXMF == 6) {
+    if (J.cnt <= 32)
+      return run_tile_mx<STAGE, 2, PF, NT>(A, J, *reinterpret_cast<SmemMx<2>*>(&sm));
+    if (J.cnt <= 64)
+      return run_tile_mx<STAGE, 4, PF, NT>(A, J, *reinterpret_cast<SmemMx<4>*>(&sm));
+    if (J.cnt <= 80)
+      return run_tile_mx<STAGE, 5, PF, NT>(A, J, *reinterpret_cast<SmemMx<5>*>(&sm));
+  }
+  run_tile_mx<STAGE, MAXMF, PF, NT>(A, J, sm);
+}
+
 template <int SF, int STAGE, int MAXMF, int PF>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_mx_kernel(FfnArgs A) {
   __shared__ __attribute__((aligned(16))) union {
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_mx_kernel(FfnArgs A
   if (J.shared)
     run_tile<SF, STAGE, MAXMF, LEAD_I4, false, false>(A, J, sm.b);
   else
-    run_tile_mx<STAGE, MAXMF, PF, NT_ROUTED>(A, J, sm.m);
+    run_routed_tile_mx<STAGE, MAXMF, PF, NT_ROUTED>(A, J, sm.m);
 }
 
 template <int SF, int MAXMF>
