@@ -135,11 +135,11 @@ def test_integer_exact_logits_and_ties():
 @pytest.mark.parametrize("T", [96, 24])
 def test_activation_rows_over_a_wide_range(T):
     """int4 layers run gate/up on fp16 MFMA, each token row scaled by its own
-    power of two (T=96: a separate fp16 copy; T=24: converted inside the
-    tiles).  Rows scaled by 2^-40 .. 2^40, an all-zero row and rows with one
-    outlier 2^20 above the rest must each match the oracle on their own scale
-    (a shared or missing scale would flush small rows or overflow big ones),
-    and the zero row must give exactly zero."""
+    power of two (T=96: 96-row tiles; T=24: 32-row tiles).  Rows scaled by
+    2^-40 .. 2^40, an all-zero row and rows with one outlier 2^20 above the
+    rest must each match the oracle on their own scale (a shared or missing
+    scale would flush small rows or overflow big ones), and the zero row must
+    give exactly zero."""
     cfg = _small_cfg("range", 13, T=T, k=4)
     inp = W.generate(cfg)
     x = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
