@@ -274,13 +274,14 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return __uint_as_float(wave_reduce_u32(__float_as_uint(v), add));
 }
 
-constexpr int TOPK_PER_LANE = MAX_EXPERTS / 64;  // 16
-
 // One wave per token; 4 tokens per 256-thread block.  Expert e lives in lane
-// e % 64, slot e / 64 (coalesced loads).  Each of the k rounds takes every
-// lane's best remaining candidate (its lowest slot among equal keys), a wave
-// max of those keys, and -- only when several lanes hold that key -- a wave
-// min of their expert ids, so equal logits go to the lower id.
+// e % 64, slot e / 64 (coalesced loads); PL slots a lane (8 for E <= 512, 16
+// for E <= 1024).  Each lane keeps its best remaining candidate (largest key,
+// lowest slot among equal keys).  Each of the k rounds takes a wave max of
+// those keys and -- only when several lanes hold that key -- a wave min of
+// their expert ids, so equal logits go to the lower id; only the winning lane
+// then rescans its slots.
+template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k,
                                                    const float* __restrict__ logits,
                                                    int32_t* __restrict__ ids,
@@ -288,22 +289,27 @@ __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  uint32_t key[TOPK_PER_LANE];
+  uint32_t key[PL];
 #pragma unroll
-  for (int j = 0; j < TOPK_PER_LANE; j++) {
+  for (int j = 0; j < PL; j++) {
     const int e = j * 64 + lane;
     key[j] = e < E ? order_key(logits[(size_t)t * E + e]) : 0u;
   }
   auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
   auto umin = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
+  uint32_t bk = 0;
+  int bj = 0;
+  auto lane_best = [&]() {
+    bk = 0;
+    bj = 0;
+#pragma unroll
+    for (int j = 0; j < PL; j++)
+      if (key[j] > bk) { bk = key[j]; bj = j; }
+  };
+  lane_best();
   int my_id = 0;
   float my_logit = 0.0f, top_logit = 0.0f;
   for (int s = 0; s < k; s++) {
-    uint32_t bk = 0;
-    int bj = 0;
-#pragma unroll
-    for (int j = 0; j < TOPK_PER_LANE; j++)
-      if (key[j] > bk) { bk = key[j]; bj = j; }
     const uint32_t m = wave_reduce_u32(bk, umax);
     const uint64_t holders = __ballot(bk == m);
     const uint32_t my_e = (uint32_t)(bj * 64 + lane);
@@ -312,10 +318,11 @@ __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k,
       e = (uint32_t)__builtin_amdgcn_readlane((int)my_e, __ffsll((long long)holders) - 1);
     else
       e = wave_reduce_u32(bk == m ? my_e : 0xFFFFFFFFu, umin);
-    if (my_e == e) {
+    if (my_e == e) {  // the winning lane drops the candidate and rescans
 #pragma unroll
-      for (int j = 0; j < TOPK_PER_LANE; j++)
+      for (int j = 0; j < PL; j++)
         if (j == bj) key[j] = 0u;
+      lane_best();
     }
     const float lg = key_to_float(m);
     if (s == 0) top_logit = lg;
@@ -331,7 +338,11 @@ __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k,
 
 hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w,
                        hipStream_t s) {
-  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(T, E, k, logits, ids, w);
+  static_assert(MAX_EXPERTS <= 16 * 64, "top-k holds at most 16 candidates a lane");
+  if (E <= 8 * 64)
+    topk_kernel<8><<<(T + 3) / 4, 256, 0, s>>>(T, E, k, logits, ids, w);
+  else
+    topk_kernel<16><<<(T + 3) / 4, 256, 0, s>>>(T, E, k, logits, ids, w);
   return hipGetLastError();
 }
 
