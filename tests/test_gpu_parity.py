@@ -83,6 +83,11 @@ def _small_cfg(name, idx, **kw):
     _small_cfg("mx_T20", 28, expert=W.MXFP4, T=20),
     _small_cfg("mx_T5_noshared", 29, expert=W.MXFP4, T=5, n_shared=0, Fs=0),
     _small_cfg("mx_E1_k1", 30, expert=W.MXFP4, E=1, k=1, n_shared=0, Fs=0, T=200),
+    # the largest widths the ABI takes (d, ffn, shared_ffn <= 16384)
+    _small_cfg("max_d_i4", 32, d=16384, F=256, Fs=256, E=4, k=2, T=40),
+    _small_cfg("max_F_i4", 33, d=256, F=16384, Fs=16384, E=4, k=2, T=40),
+    _small_cfg("max_d_mx", 34, expert=W.MXFP4, d=16384, F=256, Fs=256, E=4, k=2, T=70),
+    _small_cfg("max_F_mx", 35, expert=W.MXFP4, d=256, F=16384, Fs=16384, E=4, k=2, T=20),
 ], ids=lambda c: c.name)
 def test_small_shapes_full(cfg):
     inp = W.generate(cfg)
