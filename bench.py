@@ -165,10 +165,27 @@ def measured_peaks(torch):
     e1.record()
     torch.cuda.synchronize()
     gbs = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    # stream read: a bf16 matrix-vector product over the same 2 GiB (the
+    # vendor GEMV; the fastest plain read of the torch operations tried --
+    # reductions such as sum or amax read at 2-4 TB/s)
+    m = src.view(torch.bfloat16).view(32768, -1)
+    vec = torch.ones(m.shape[1], dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        torch.mv(m, vec)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.mv(m, vec)
+    e1.record()
+    torch.cuda.synchronize()
+    rgbs = src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, m, vec
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": round(tflops, 1), "hbm_copy_gbs": round(gbs, 1),
-            "how": "torch.mm bf16 8192^3; 2 GiB device-to-device copy, read + write bytes"}
+            "hbm_read_gbs": round(rgbs, 1),
+            "how": "torch.mm bf16 8192^3; 2 GiB device-to-device copy, read + write bytes; "
+                   "torch.mv bf16 over a 2 GiB matrix, bytes read"}
 
 
 def algorithmic(cfg, T, n_active):
@@ -513,7 +530,7 @@ def main():
     if roof_p is not None:
         roof_p["frac_of_measured_peak"] = round(roof_p["achieved"] / peaks["mfma_bf16_tflops"], 4)
     if roof_d is not None:
-        roof_d["frac_of_measured_peak"] = round(roof_d["achieved"] / peaks["hbm_copy_gbs"], 4)
+        roof_d["frac_of_measured_peak"] = round(roof_d["achieved"] / peaks["hbm_read_gbs"], 4)
     if prefill is not None:
         line["prefill"] = _r(prefill)
     if decode is not None:
