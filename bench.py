@@ -473,6 +473,9 @@ def main():
         return
     if args.workload == "mxfp4":
         mx = run_mxfp4(args, torch, W)
+        peaks = measured_peaks(torch)
+        mx["decode_roofline"]["frac_of_measured_peak"] = round(
+            mx["decode_roofline"]["achieved"] / peaks["hbm_read_gbs"], 4)
         print(json.dumps({"metric": "MoE-layer tokens/s with MXFP4 W4A4 routed experts (T=4096 "
                                     "prefill; T=16 and T=32 decode)",
                           "unit": "tokens/s", "n_gpus": 1, "data": "synthetic", "dtype": "fp4",
@@ -482,6 +485,7 @@ def main():
                                                  "MXFP4-quantized per 32",
                                      "shared_w": "int8 per-row fp16 scales, bf16 activations"},
                           "peaks": {"fp4_mfma_tflops": FP4_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS},
+                          "measured_peaks": peaks,
                           "mxfp4": _r(mx)}), flush=True)
         return
     prefill = decode = roof_p = roof_d = pre_inputs = None
