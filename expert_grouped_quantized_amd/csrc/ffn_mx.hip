@@ -4,8 +4,9 @@
 // expert 16-bit), in the OCP Microscaling FP4 format that CDNA4's scaled
 // MFMA (16x16x128, e2m1 operands, one E8M0 scale per 32 K per row) consumes.
 //
-//   x_to_mx_kernel   each token row of x -> e2m1 codes + E8M0 scales, block by
-//                    block of 32 (OCP MX rule), into the workspace
+//   x_to_mx_kernel   x, gathered into route-plan order (row p = token
+//                    perm[p] / k) -> e2m1 codes + E8M0 scales, block by block
+//                    of 32 (OCP MX rule), into the workspace
 //   ffn_mx_kernel<1> routed tiles: g, u = Wg xq, Wu xq on the FP4 MFMA;
 //                    h = w * silu(g) * u in fp32, quantized per row and 32 h
 //                    columns (one wave's columns) -> hq, hsc
@@ -20,6 +21,14 @@
 // and the block stages the tile rows' codes (64 bytes a row) and scales
 // through LDS, double-buffered.  No dequantization: codes and scales feed the
 // MFMA as they are.
+//
+// Activation layout (x's codes and h's codes, both in route-plan row order,
+// n = T*k rows): chunk-major, so the rows of a tile are contiguous in every
+// 128-K chunk --
+//   codes   q[(kc * n + p) * 64 + kb * 16 + j]   chunk kc, row p, 32-K block kb
+//   scales  s[((kc / 2) * n + p) * 8 + (kc % 2) * 4 + kb]   (pairs of chunks)
+// The gate/up epilogue of column block nb writes chunk nb of h (its 128 h
+// columns) whole.
 #include <utility>
 
 #include "ffn_kernels.h"
@@ -68,17 +77,25 @@ __device__ __forceinline__ int mx_exponent(uint32_t amax_bits, float* inv) {
 }
 
 // ---- x -> MXFP4 --------------------------------------------------------------
-// One thread per 32-element block of a row: 64 bytes of bf16 in, 16 bytes of
-// codes and one scale byte out.
-__global__ __launch_bounds__(256) void x_to_mx_kernel(int T, int d, const uint16_t* __restrict__ x,
+// One thread per 32-element block: thread g takes block kb = g % 4 of chunk kc
+// of plan row p ((g / 4) = kc * n + p), so four threads read 256 contiguous
+// bytes of the token's row and write one row's 64 code bytes, and successive
+// rows follow each other in the output.  A token's row is quantized once per
+// assignment (k times), to the same codes.
+__global__ __launch_bounds__(256) void x_to_mx_kernel(int n, int k, int d,
+                                                      const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ perm,
                                                       uint8_t* __restrict__ xq,
                                                       uint8_t* __restrict__ xsc) {
-  const int nb = d / 32;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= (int64_t)T * nb) return;
-  const int64_t t = g / nb;
-  const int b = (int)(g - t * nb);
-  const u32x4_t* src = (const u32x4_t*)(x + t * d + b * 32);
+  const int64_t nblk = (int64_t)n * (d / 32);
+  if (g >= nblk) return;
+  const int kb = (int)(g & 3);
+  const int64_t cp = g >> 2;  // kc * n + p
+  const int kc = (int)(cp / n);
+  const int p = (int)(cp - (int64_t)kc * n);
+  const int64_t t = perm[p] / k;
+  const u32x4_t* src = (const u32x4_t*)(x + t * d + (kc * 4 + kb) * 32);
   u32x4_t v[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) v[j] = src[j];
@@ -100,8 +117,8 @@ __global__ __launch_bounds__(256) void x_to_mx_kernel(int T, int d, const uint16
     c = cvt_fp4x2<3>(c, bf16_lo(v[j][3]) * inv, bf16_hi(v[j][3]) * inv);
     o[j] = c;
   }
-  *(u32x4_t*)(xq + t * (d / 2) + b * 16) = o;
-  xsc[t * nb + b] = (uint8_t)(E + 127);
+  *(u32x4_t*)(xq + cp * 64 + kb * 16) = o;
+  xsc[((int64_t)(kc >> 1) * n + p) * 8 + (kc & 1) * 4 + kb] = (uint8_t)(E + 127);
 }
 
 // ---- weight registers of one MXFP4 wave tile (64 rows x 128 K) -------------
@@ -133,7 +150,6 @@ struct SmemMx {
   uint8_t a[2][MAXMF * 16 * 64];
   uint8_t s[2][4 * 16 * 8];
   float wrow[MAXMF * 16];
-  int src[MAXMF * 16];
 };
 
 // Stage-1 epilogue: h = w * silu(g) * u of the wave's 32 h columns, quantized
@@ -144,7 +160,7 @@ struct SmemMx {
 // bytes (two columns) of two rows.  The block's codes (64 bytes a row: 16 per
 // wave) and scales (4 bytes a row) are gathered in LDS (`hl`, `sl`, free after
 // the K loop) and leave as one 16-byte store per row piece and one 4-byte
-// store per row: hq is row-major (F/2 bytes a row), hsc F/32 bytes a row.
+// store per row, into chunk nb of the plan-order chunk-major layout.
 template <int NMF, typename RowW>
 __device__ __forceinline__ void store_h_mx(const FfnArgs& A, int start, int cnt, int nb,
                                            const f32x4_t (&acc)[NMF][4], RowW wrow, uint8_t* hl,
@@ -197,16 +213,15 @@ __device__ __forceinline__ void store_h_mx(const FfnArgs& A, int start, int cnt,
     if (c < 4) sl[(i * 16 + quad + c) * 4 + wave] = (uint8_t)(c == 0 ? eb[0] : c == 1 ? eb[1] : c == 2 ? eb[2] : eb[3]);
   }
   __syncthreads();
-  const size_t qs = (size_t)A.F / 2, ss = (size_t)A.F / 32;
+  // chunk nb of h: the tile's rows are contiguous (plan-order chunk-major)
+  const size_t n = (size_t)A.T * A.k;
+  uint8_t* hq = A.hq + ((size_t)nb * n + start) * 64;
 #pragma unroll
-  for (int q = tid; q < ROWS * 4; q += WAVES * 64) {
-    const int row = q >> 2, part = q & 3;
-    if (row < cnt)
-      *(u32x4_t*)(A.hq + (size_t)(start + row) * qs + nb * 64 + part * 16) =
-          *(const u32x4_t*)(hl + row * 64 + part * 16);
-  }
+  for (int q = tid; q < ROWS * 4; q += WAVES * 64)
+    if ((q >> 2) < cnt) *(u32x4_t*)(hq + q * 16) = *(const u32x4_t*)(hl + q * 16);
   if (tid < ROWS && tid < cnt)
-    *(uint32_t*)(A.hsc + (size_t)(start + tid) * ss + nb * 4) = *(const uint32_t*)(sl + tid * 4);
+    *(uint32_t*)(A.hsc + ((size_t)(nb >> 1) * n + start + tid) * 8 + (nb & 1) * 4) =
+        *(const uint32_t*)(sl + tid * 4);
 }
 
 // One routed (row tile, column block) of an MXFP4 layer.
@@ -227,44 +242,30 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   const uint8_t* sect = STAGE == 1 ? blob : blob + w1_bytes(MOE_MXFP4, A.d, A.F);
   const uint8_t* wnext = sect + (size_t)run * nk * TILE_BYTES_MX4;
 
-  for (int m = tid; m < ROWS; m += WAVES * 64) {
-    int src = -1;
-    float wf = 0.0f;
-    if (m < J.cnt) {
-      if (STAGE == 1) {
-        const int f = A.perm[J.start + m];
-        src = f / A.k;
-        wf = A.topk_w[f];
-      } else {
-        src = J.start + m;
-      }
-    }
-    sm.src[m] = src;
-    sm.wrow[m] = wf;
-  }
+  // folded router weight of each tile row (gate/up)
+  for (int m = tid; m < ROWS; m += WAVES * 64)
+    sm.wrow[m] = (STAGE == 1 && m < J.cnt) ? A.topk_w[A.perm[J.start + m]] : 0.0f;
   __syncthreads();
 
-  // Rows past the tile's end read the tile's first row (never stored).
-  const uint8_t* qbase = STAGE == 1 ? A.xq : A.hq;
-  const uint8_t* sbase = STAGE == 1 ? A.xsc : A.hsc;
-  const size_t qstride = (size_t)K / 2, sstride = (size_t)K / 32;
+  // A rows are plan rows start .. start + cnt - 1 of the chunk-major layout
+  // (x's codes for gate/up, h's for down).  Rows past the tile's end read
+  // the tile's first row (never stored).
+  const size_t n = (size_t)A.T * A.k;
+  const size_t qstep = n * 64, sstep = n * 8;  // one chunk of codes, one chunk pair of scales
+  const uint8_t* qbase = (STAGE == 1 ? A.xq : A.hq) + (size_t)J.start * 64;
+  const uint8_t* sbase = (STAGE == 1 ? A.xsc : A.hsc) + (size_t)J.start * 8;
   const uint8_t* aq[PPT];
   int aq_lds[PPT];
 #pragma unroll
   for (int j = 0; j < PPT; j++) {
     const int q = (tid + WAVES * 64 * j) % PIECES;  // piece q: row q / 4, K block q % 4
     const int r = q >> 2, kb = q & 3;
-    const int s = sm.src[r] >= 0 ? sm.src[r] : sm.src[0];
-    aq[j] = qbase + (size_t)s * qstride + kb * 16;
+    aq[j] = qbase + (r < J.cnt ? r : 0) * 64 + kb * 16;
     aq_lds[j] = mx_lds_index(r, kb);
   }
   // scales: thread tid stages row tid % ROWS (4 bytes a chunk)
   const int srow = tid % ROWS;
-  const uint8_t* as;
-  {
-    const int s = sm.src[srow] >= 0 ? sm.src[srow] : sm.src[0];
-    as = sbase + (size_t)s * sstride;
-  }
+  const uint8_t* as = sbase + (srow < J.cnt ? srow : 0) * 8;
   const int s_lds = (srow & 15) * 8 + (srow >> 4);  // + kb * 128
 
   f32x4_t acc[NMF][4];
@@ -275,7 +276,7 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
 
   // Ring slot p holds chunk kc with kc % 2 == p.  The scales of an even chunk
   // and the next one arrive together in `apair` (one 8-byte load per row
-  // every two chunks; K/32 is a multiple of 8, so the pair is aligned).
+  // every two chunks).
   u32x4_t areg[PF][PPT];
   uint2 apair;
   // Small tiles have fewer pieces than threads: only the threads that own a
@@ -287,8 +288,8 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   auto load_a = [&](int kc, int p) {
 #pragma unroll
     for (int j = 0; j < PPT; j++)
-      if (own0) areg[p][j] = *(const u32x4_t*)(aq[j] + kc * (KC_MX / 2));
-    if (p == 0 && own_s) apair = *(const uint2*)(as + kc * 4);
+      if (own0) areg[p][j] = *(const u32x4_t*)(aq[j] + (size_t)kc * qstep);
+    if (p == 0 && own_s) apair = *(const uint2*)(as + (size_t)(kc >> 1) * sstep);
   };
   auto store_a = [&](int buf, int p, uint32_t sc) {
 #pragma unroll
@@ -413,9 +414,10 @@ static hipError_t launch_mx_stages(const FfnArgs& a0, hipStream_t s) {
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
   const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
   const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
-  const int64_t blocks = (int64_t)a.T * (a.d / 32);
+  const int n = a.T * a.k;
+  const int64_t blocks = (int64_t)n * (a.d / 32);
   x_to_mx_kernel<<<(unsigned)((blocks + 255) / 256), 256, 0, s>>>(
-      a.T, a.d, (const uint16_t*)a.hidden, a.xq, a.xsc);
+      n, a.k, a.d, (const uint16_t*)a.hidden, a.perm, a.xq, a.xsc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ffn_mx_kernel<SF, 1, MAXMF, LEAD_MX><<<slots * nb1, WAVES * 64, 0, s>>>(a);

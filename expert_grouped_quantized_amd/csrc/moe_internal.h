@@ -100,13 +100,13 @@ struct WsLayout {
   size_t ntiles;       // int32 [1]             routed row tiles in the plan
   size_t tiles;        // int2  [routed_slots]  (expert, first row) per tile
   size_t h_routed;     // act-typed [T*k, F]    intermediate h, permuted rows
-                       //   (MXFP4 layers: e2m1 codes [T*k, F/2])
+                       //   (MXFP4 layers: e2m1 codes [T*k, F/2], chunk-major)
   size_t h_scale;      // MXFP4 layers: E8M0 [T*k, F/32], the scales of h
   size_t h_shared;     // act-typed [T, Fs]     intermediate h of the shared expert
   size_t x16;          // fp16 [T, d]           activations scaled by 2^-xexp[t] (int4 path)
-                       //   (MXFP4 layers: e2m1 codes of x [T, d/2])
+                       //   (MXFP4 layers: e2m1 codes of x in plan order [T*k, d/2])
   size_t xexp;         // float [T]             2^xexp[t], the scale to undo
-                       //   (MXFP4 layers: E8M0 [T, d/32], the scales of x)
+                       //   (MXFP4 layers: E8M0 [T*k, d/32], the scales of x)
   size_t total;
 };
 
@@ -128,8 +128,8 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   L.h_scale = off;  off = align256(off + (mx ? (size_t)n * (D.ffn / 32) : 0));
   L.h_shared = off; off = align256(off + (D.n_shared ? (size_t)T * D.shared_ffn * elem : 0));
   const bool x16 = D.act == MOE_BF16 && ig32_bits(D.expert_w) != 0;
-  L.x16 = off;      off = align256(off + (x16 ? (size_t)T * D.d * 2 : mx ? (size_t)T * D.d / 2 : 0));
-  L.xexp = off;     off = align256(off + (x16 ? (size_t)T * 4 : mx ? (size_t)T * (D.d / 32) : 0));
+  L.x16 = off;      off = align256(off + (x16 ? (size_t)T * D.d * 2 : mx ? (size_t)n * D.d / 2 : 0));
+  L.xexp = off;     off = align256(off + (x16 ? (size_t)T * 4 : mx ? (size_t)n * (D.d / 32) : 0));
   L.total = off;
   return L;
 }
