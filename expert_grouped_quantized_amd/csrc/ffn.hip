@@ -1,5 +1,6 @@
 // ffn.hip -- launches of the expert-grouped SwiGLU GEMMs for bf16 and int4
-// routed weights, the fp16 activation copy of int4 layers, and the fp32 path.
+// routed weights (other code widths: ffn_lowbit.hip; MXFP4: ffn_mx.hip), the
+// fp16 activation copy of int4 and b-bit layers, and the fp32 path.
 #include "ffn_kernels.h"
 
 namespace moe {

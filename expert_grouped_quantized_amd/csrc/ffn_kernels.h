@@ -13,12 +13,15 @@
 // LDS, 64 K at a time, double-buffered, and read as MFMA A operands by all 4
 // waves.  Weights stream straight from HBM into each wave's registers in the
 // tile order moe_pack_experts wrote them (one contiguous run per wave), PF
-// chunks ahead, are dequantized in registers to bf16 (int4: code * fp16 group
-// scale, rounded to nearest even; int8: the exact code, its row scale applied
-// to the fp32 accumulator), and feed bf16 MFMA 16x16x32 with fp32
-// accumulation.  A wave covers all rows of its tile, so each weight is read
-// and dequantized once per row tile; 16-row MFMA fragments past the tile's
-// last row are skipped.
+// chunks ahead, and are dequantized in registers: to fp16 for the gate/up
+// products of int4 and b-bit layers (which run fp16 MFMA on an fp16 copy of
+// x), to bf16 otherwise (codes times the fp16 group scale, rounded to nearest
+// even; int8 codes enter exactly and their row scale multiplies the fp32
+// accumulator); MFMA 16x16x32 with fp32 accumulation.  A wave covers all rows
+// of its tile, so each weight is read and dequantized once per row tile.  A
+// tile runs a body built for just enough 16-row fragments (run_routed_tile);
+// fragments past its last row compute copies of its first row and are never
+// stored.
 #pragma once
 
 #include "wave_tile.h"
