@@ -50,7 +50,9 @@ struct WTile<MOE_BF16> {
 #pragma unroll
     for (int j = 0; j < 8; j++) v[j] = ldw<NT>(t, j * 64 + lane);
   }
-  __device__ __forceinline__ u32x4_t frag(int f, int s) const { return v[f * 2 + s]; }
+  __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
+    return v[f * 2 + s];
+  }
   template <bool>
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     return v[f * 2 + s];  // never used: bf16 weights run bf16 MFMA
@@ -75,18 +77,22 @@ struct WTile<MOE_I4_G32> {
     const uint32_t sw = sc[si >> 1];
     return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
   }
-  // bf16(code * scale): code + 8 as a float, one FMA with the scale (exact in
-  // fp32), rounded to nearest even by the pack
-  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
-    const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
-    const float bias = -8.0f * scale;
+  // bf16(code * scale): a nibble pair OR-ed under the fp16 exponent of 1024
+  // reads as 1024 + code + 8 each; one mixed-precision FMA per half takes it
+  // with the fp16 scale and -1032 * scale (both products exact in fp32, so the
+  // sum is code * scale exactly) and the pack rounds to nearest even.  Two
+  // VALU ops per nibble pair fewer than a byte convert per code.
+  __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts& k) const {
+    const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)scale_bits(f, s));
+    const float scale = (float)sh;
+    const float bias = -1032.0f * scale;
     const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
-    const uint32_t lo = q & 0x0f0f0f0fu, hi = (q >> 4) & 0x0f0f0f0fu;
     u32x4_t r;
-    r[0] = pack_bf16x2(fmaf(ubyte0_f(lo), scale, bias), fmaf(ubyte2_f(lo), scale, bias));
-    r[1] = pack_bf16x2(fmaf(ubyte0_f(hi), scale, bias), fmaf(ubyte2_f(hi), scale, bias));
-    r[2] = pack_bf16x2(fmaf(ubyte1_f(lo), scale, bias), fmaf(ubyte3_f(lo), scale, bias));
-    r[3] = pack_bf16x2(fmaf(ubyte1_f(hi), scale, bias), fmaf(ubyte3_f(hi), scale, bias));
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), k.lo, k.magic));
+      r[j] = pack_bf16x2(fmaf((float)t[0], scale, bias), fmaf((float)t[1], scale, bias));
+    }
     return r;
   }
   // fp16(code * scale): a nibble pair OR-ed into two fp16 mantissas is
@@ -134,7 +140,7 @@ struct WTile<MOE_I8_ROW> {
 #pragma unroll
     for (int j = 0; j < 4; j++) v[j] = ldw<NT>(t, j * 64 + lane);
   }
-  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+  __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
     const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
     u32x4_t r;
     r[0] = pack_bf16x2(sbyte0_f(w0), sbyte1_f(w0));
@@ -227,7 +233,7 @@ struct WTileB {
   }
   // bf16(code * scale): code + 2^(b-1) as a float, one FMA with the scale
   // (exact in fp32), rounded to nearest even by the pack
-  __device__ __forceinline__ u32x4_t frag(int f, int s) const {
+  __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
     const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
     const float bias = -(float)(1 << (B - 1)) * scale;
     const int base = (2 * f + s) * 8 * B;
