@@ -584,8 +584,7 @@ moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* 
   a.routed_slots = L.routed_slots;
   a.shared_slots = D->n_shared ? (T + BM - 1) / BM : 0;
   a.hidden = hidden; a.topk_w = topk_w; a.offsets = offsets; a.perm = perm;
-  a.ntiles = (const int32_t*)(w + L.ntiles);
-  a.tiles = (const int2*)(w + L.tiles);
+  a.tiles = (const int4*)(w + L.tiles);
   a.routed_blob = (const uint8_t*)routed_blob;
   a.shared_blob = (const uint8_t*)shared_blob;
   a.h_routed = w + L.h_routed; a.h_shared = w + L.h_shared;

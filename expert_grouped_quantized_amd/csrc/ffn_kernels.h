@@ -51,14 +51,15 @@ struct TileCtx {
   const uint16_t* arow[3];
 };
 
+// Lead of the loads, in K chunks: 4 for int4 and 2-bit codes (the bytes of the
+// call); 2 for bf16 tiles (4x the bytes and registers of an int4 tile), int8
+// shared tiles (re-read from cache by every row tile) and the 3- and 5- to
+// 8-bit codes (their registers).
 template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
 __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm,
-                                          const TileCtx& C) {
+                                          const TileCtx& C,
+                                          WTile<FMT> (&ring)[lead_of(FMT, PF_MAX)]) {
   constexpr int NMF = MAXMF;
-  // Lead of the loads, in K chunks: 4 for int4 and 2-bit codes (the bytes of
-  // the call); 2 for bf16 tiles (4x the bytes and registers of an int4 tile),
-  // int8 shared tiles (re-read from cache by every row tile) and the 3- and
-  // 5- to 8-bit codes (their registers).
   constexpr int PF = lead_of(FMT, PF_MAX);
   constexpr int ROWS = MAXMF * 16;
   constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
@@ -120,13 +121,15 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
   // it, and PF chunks stay in flight.  nk is a multiple of PF (the ABI's width
   // checks).
   static_assert(PF == 2 || PF == 4, "load lead must be 2 or 4 chunks");
-  WTile<FMT> ring[PF];
-  const uint8_t* wnext = C.wt;
+  // stage 1: the caller issued the first PF weight chunks
+  const uint8_t* wnext = C.wt + (STAGE == 1 ? PF * tb : 0);
 #pragma unroll
   for (int p = 0; p < PF; p++) {
     load_a(p, areg[p]);
-    ring[p].template load<NT>(wnext, lane);
-    wnext += tb;
+    if constexpr (STAGE != 1) {
+      ring[p].template load<NT>(wnext, lane);
+      wnext += tb;
+    }
   }
   store_a(sm.a[0], areg[0]);
   __syncthreads();
@@ -184,25 +187,37 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
   C.sect = STAGE == 1 ? blob : blob + w1_bytes(FMT, A.d, C.Fw);
   C.wt = C.sect + (size_t)C.run * C.nk * tb;
 
-  // rows of this tile: source row of the activations and folded router weight
-  for (int m = tid; m < ROWS; m += WAVES * 64) {
-    int src = -1;
-    float wf = 0.0f, xs = 1.0f;
-    if (m < J.cnt) {
-      if (STAGE == 1) {
-        if (J.shared) {
-          src = J.start + m;
-          wf = 1.0f;
-        } else {
-          const int f = A.perm[J.start + m];
-          src = f / A.k;
-          wf = A.topk_w[f];
-        }
-        if (F16) xs = A.xscale[src];
-      } else {
+  // Rows of this tile (thread m < ROWS has row m): source row of the
+  // activations, folded router weight, fp16 row scale.  In stage 1 the first
+  // PF weight chunks, which depend only on the expert, are issued right after
+  // the row loads (so waiting for those does not wait for weights) instead of
+  // after the row barrier; stage 2 rows need no loads.
+  static_assert(ROWS <= WAVES * 64, "one row per thread");
+  const int m = tid;
+  int src = -1;
+  float wf = 0.0f, xs = 1.0f;
+  if (m < ROWS && m < J.cnt) {
+    if (STAGE == 1) {
+      if (J.shared) {
         src = J.start + m;
+        wf = 1.0f;
+      } else {
+        const int f = A.perm[J.start + m];
+        src = f / A.k;
+        wf = A.topk_w[f];
       }
+      if (F16) xs = A.xscale[src];
+    } else {
+      src = J.start + m;
     }
+  }
+  constexpr int PF = lead_of(FMT, PF_MAX);
+  WTile<FMT> ring[PF];
+  if constexpr (STAGE == 1) {
+#pragma unroll
+    for (int p = 0; p < PF; p++) ring[p].template load<NT>(C.wt + p * tb, tid & 63);
+  }
+  if (m < ROWS) {
     sm.src[m] = src;
     sm.wrow[m] = wf;
     sm.xs[m] = xs;
@@ -221,7 +236,7 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
     const int s = sm.src[r] >= 0 ? sm.src[r] : sm.src[0];
     C.arow[j] = abase + (size_t)s * astride + (q & 7) * 8;
   }
-  tile_body<FMT, STAGE, MAXMF, PF_MAX, F16, NT>(A, J, sm, C);
+  tile_body<FMT, STAGE, MAXMF, PF_MAX, F16, NT>(A, J, sm, C, ring);
 }
 
 // A routed tile of a 96-row kernel with fewer rows runs a body with fewer row
@@ -254,12 +269,12 @@ __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_r
   const int slot = (b / (8 * NB)) * 8 + (b & 7);
   J.nb = (b >> 3) % NB;
   if (slot < A.routed_slots) {
-    if (slot >= *A.ntiles) return false;
-    const int2 t = A.tiles[slot];
+    const int4 t = A.tiles[slot];  // one scalar load: (expert, first row, rows)
+    if (t.z == 0) return false;
     J.shared = false;
     J.expert = t.x;
-    J.start = A.offsets[t.x] + t.y;
-    J.cnt = min(rows_per_tile, A.offsets[t.x + 1] - J.start);
+    J.start = t.y;
+    J.cnt = min(rows_per_tile, t.z);
     return J.nb < ncols_routed;
   }
   const int s = slot - A.routed_slots;

@@ -44,7 +44,7 @@ constexpr int TILE_BYTES_MX4 = 64 * 128 / 2 + 64 * 4;  // 4352
 constexpr int LEAD_MX = 2;
 
 // ---- route plan ----------------------------------------------------------
-constexpr int PLAN_CHUNK = 4096;   // assignments per block of the plan kernels
+constexpr int PLAN_CHUNK = 1024;   // assignments per block of the plan kernels
 constexpr int PLAN_THREADS = 1024; // 16 waves
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 32;
@@ -97,8 +97,8 @@ struct WsLayout {
   int n_chunks;        // plan blocks
   int routed_slots;    // upper bound on routed row tiles
   size_t counts;       // int32 [n_chunks][E]   per-chunk expert histogram
-  size_t ntiles;       // int32 [1]             routed row tiles in the plan
-  size_t tiles;        // int2  [routed_slots]  (expert, first row) per tile
+  size_t tiles;        // int4  [routed_slots]  (expert, first row, rows, 0) per
+                       //                       tile; rows 0 past the plan's tiles
   size_t h_routed;     // act-typed [T*k, F]    intermediate h, permuted rows
                        //   (MXFP4 layers: e2m1 codes [T*k, F/2], chunk-major)
   size_t h_scale;      // MXFP4 layers: E8M0 [T*k, F/32], the scales of h
@@ -121,8 +121,7 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   size_t elem = D.act == MOE_F32 ? 4 : 2;
   size_t off = 0;
   L.counts = off;   off = align256(off + (size_t)L.n_chunks * D.n_experts * 4);
-  L.ntiles = off;   off = align256(off + 4);
-  L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 8);
+  L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 16);
   const bool mx = D.act == MOE_BF16 && D.expert_w == MOE_MXFP4;
   L.h_routed = off; off = align256(off + (size_t)n * D.ffn * (mx ? 1 : 2 * elem) / 2);
   L.h_scale = off;  off = align256(off + (mx ? (size_t)n * (D.ffn / 32) : 0));
@@ -152,8 +151,7 @@ struct FfnArgs {
   const float* topk_w;
   const int32_t* offsets;
   const int32_t* perm;
-  const int32_t* ntiles;
-  const int2* tiles;
+  const int4* tiles;
   const uint8_t* routed_blob;
   const uint8_t* shared_blob;
   void* h_routed;

@@ -5,7 +5,8 @@
 // offsets = exclusive prefix sum of the expert histogram; perm = a stable
 // counting sort of the flat assignment index f = t*k + s by expert (ascending f
 // inside each expert); inv_perm its inverse.  The input is cut into chunks of
-// PLAN_CHUNK assignments, one 1024-thread block each:
+// PLAN_CHUNK (= the block size, so one rank pass each) assignments, one
+// 1024-thread block each:
 //   plan_count   : per-chunk histogram in LDS -> counts[chunk][E]
 //   plan_scatter : totals and per-chunk bases from counts (fixed order), block
 //                  scan -> offsets; stable in-chunk ranks from wave ballots
@@ -64,7 +65,7 @@ template <bool SINGLE>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     int n, int E, int n_chunks, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv_perm, int32_t* __restrict__ ntiles, int2* __restrict__ tiles) {
+    int32_t* __restrict__ inv_perm, int slots, int4* __restrict__ tiles) {
   __shared__ int run[MAX_EXPERTS];
   __shared__ int hist[MAX_EXPERTS];
   __shared__ __attribute__((aligned(16))) uint8_t wcnt[PLAN_WAVES][MAX_EXPERTS];
@@ -82,12 +83,27 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     for (int i = tid; i < len; i += PLAN_THREADS) atomicAdd(&hist[ids[base + i]], 1);
     __syncthreads();
     if (tid < E) total = hist[tid];
-  } else if (tid < E) {
-    for (int c = 0; c < n_chunks; c++) {
-      int v = counts[(size_t)c * E + tid];
-      if (c < chunk) before += v;
-      total += v;
+  } else {
+    // PLAN_THREADS / E threads per expert each sum every r-th chunk's count;
+    // the parts are then added through LDS (integer sums: order-free)
+    const int r = PLAN_THREADS / E, e = tid % E, part = tid / E;
+    if (part < r) {
+      for (int c = part; c < n_chunks; c += r) {
+        const int v = counts[(size_t)c * E + e];
+        if (c < chunk) before += v;
+        total += v;
+      }
     }
+    hist[tid] = total;
+    run[tid] = before;
+    __syncthreads();
+    if (tid < E) {
+      for (int q = 1; q < r; q++) {
+        total += hist[tid + q * E];
+        before += run[tid + q * E];
+      }
+    }
+    __syncthreads();
   }
   // 2) offsets
   const int off = block_exclusive_scan(tid < E ? total : 0, wsum, &total_all);
@@ -95,11 +111,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
   if (chunk == 0) {
     if (tid < E) offsets[tid] = off;
     if (tid == 0) offsets[E] = n;
-    // 3) row tiles of the grouped GEMMs: expert e owns ceil(total/BM) tiles
+    // 3) row tiles of the grouped GEMMs: expert e owns ceil(total/BM) tiles,
+    //    each stored resolved (expert, first row, rows) so a GEMM block finds
+    //    its rows with one load; the slots past the plan's tiles hold 0 rows
     const int nt = tid < E ? (total + BM - 1) / BM : 0;
     const int tstart = block_exclusive_scan(nt, wsum, &total_all);
-    for (int j = 0; j < nt; j++) tiles[tstart + j] = make_int2(tid, j * BM);
-    if (tid == 0) *ntiles = total_all;
+    for (int j = 0; j < nt; j++)
+      tiles[tstart + j] = make_int4(tid, off + j * BM, min(BM, total - j * BM), 0);
+    for (int j = total_all + tid; j < slots; j += PLAN_THREADS) tiles[j] = make_int4(0, 0, 0, 0);
   }
   __syncthreads();
 
@@ -147,17 +166,16 @@ hipError_t launch_plan(int n, int E, const int32_t* ids, int32_t* offsets, int32
                        int32_t* inv_perm, void* ws, const WsLayout& L, hipStream_t s) {
   uint8_t* w = (uint8_t*)ws;
   int32_t* counts = (int32_t*)(w + L.counts);
-  int32_t* ntiles = (int32_t*)(w + L.ntiles);
-  int2* tiles = (int2*)(w + L.tiles);
+  int4* tiles = (int4*)(w + L.tiles);
   if (L.n_chunks == 1) {
     plan_scatter_kernel<true><<<1, PLAN_THREADS, 0, s>>>(n, E, 1, ids, counts, offsets, perm,
-                                                         inv_perm, ntiles, tiles);
+                                                         inv_perm, L.routed_slots, tiles);
   } else {
     plan_count_kernel<<<L.n_chunks, PLAN_THREADS, 0, s>>>(n, E, ids, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     plan_scatter_kernel<false><<<L.n_chunks, PLAN_THREADS, 0, s>>>(
-        n, E, L.n_chunks, ids, counts, offsets, perm, inv_perm, ntiles, tiles);
+        n, E, L.n_chunks, ids, counts, offsets, perm, inv_perm, L.routed_slots, tiles);
   }
   return hipGetLastError();
 }
