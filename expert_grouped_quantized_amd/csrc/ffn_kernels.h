@@ -106,7 +106,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
         av[i] = *(const u32x4_t*)(as + lds_a_index(i * 16 + (lane & 15), ch));
 #pragma unroll
       for (int f = 0; f < 4; f++) {
-        const u32x4_t b = F16 ? w.template frag16<(MAXMF <= 2)>(f, s, f16k) : w.frag(f, s, f16k);
+        const u32x4_t b = F16 ? w.frag16(f, s, f16k) : w.frag(f, s, f16k);
 #pragma unroll
         for (int i = 0; i < NMF; i++)
           acc[i][f] = F16 ? mfma16x16_f16(av[i], b, acc[i][f]) : mfma16x16(av[i], b, acc[i][f]);

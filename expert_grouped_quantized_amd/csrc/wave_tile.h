@@ -53,7 +53,6 @@ struct WTile<MOE_BF16> {
   __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
     return v[f * 2 + s];
   }
-  template <bool>
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     return v[f * 2 + s];  // never used: bf16 weights run bf16 MFMA
   }
@@ -98,36 +97,26 @@ struct WTile<MOE_I4_G32> {
   // fp16(code * scale): a nibble pair OR-ed into two fp16 mantissas is
   // (1024 + code + 8) each; one packed subtract makes the codes exact, one
   // packed multiply by the fp16 scale rounds each product to nearest even.
-  // ONE_SHIFT (used where registers are plentiful) takes the pairs held in
-  // the high nibbles of bytes 0 and 2 in place, as 1024 + 16 (code + 8), and
-  // makes them exact with one packed fma by 1/16 and -72 instead of a shift:
-  // one shift per dword instead of three, the same results bit for bit.
-  template <bool ONE_SHIFT>
+  // The pairs held in the high nibbles of bytes 0 and 2 are taken in place,
+  // as 1024 + 16 (code + 8), and made exact with one packed fma by 1/16 and
+  // -72 instead of a shift: one shift per dword instead of three.
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts& k) const {
     const uint32_t sb = scale_bits(f, s);
     const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
     const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
     const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
+    const uint32_t q8 = q >> 8;
+    const f16x2_t t0 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.lo, k.magic));
+    const f16x2_t t1 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.hi, k.magic));
+    const f16x2_t t2 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.lo, k.magic));
+    const f16x2_t t3 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.hi, k.magic));
     u32x4_t r;
-    if constexpr (ONE_SHIFT) {
-      const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-      const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
-      const uint32_t q8 = q >> 8;
-      const f16x2_t t0 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.lo, k.magic));
-      const f16x2_t t1 = __builtin_bit_cast(f16x2_t, and_or_b32(q, k.hi, k.magic));
-      const f16x2_t t2 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.lo, k.magic));
-      const f16x2_t t3 = __builtin_bit_cast(f16x2_t, and_or_b32(q8, k.hi, k.magic));
-      r[0] = __builtin_bit_cast(uint32_t, (t0 + off) * s2);
-      r[1] = __builtin_bit_cast(uint32_t, (t1 * sixteenth + off16) * s2);
-      r[2] = __builtin_bit_cast(uint32_t, (t2 + off) * s2);
-      r[3] = __builtin_bit_cast(uint32_t, (t3 * sixteenth + off16) * s2);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), k.lo, k.magic));
-        r[j] = __builtin_bit_cast(uint32_t, (t + off) * s2);
-      }
-    }
+    r[0] = __builtin_bit_cast(uint32_t, (t0 + off) * s2);
+    r[1] = __builtin_bit_cast(uint32_t, (t1 * sixteenth + off16) * s2);
+    r[2] = __builtin_bit_cast(uint32_t, (t2 + off) * s2);
+    r[3] = __builtin_bit_cast(uint32_t, (t3 * sixteenth + off16) * s2);
     return r;
   }
 };
@@ -154,7 +143,6 @@ struct WTile<MOE_I8_ROW> {
   // reads as 1024 + code + 128, and one packed subtract of 1152 leaves the
   // code.  (All compiler-visible ops: the MFMA that reads the result right
   // after gets its hazard wait states.)
-  template <bool>
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     const uint32_t w0 = v[f][2 * s] ^ 0x80808080u, w1 = v[f][2 * s + 1] ^ 0x80808080u;
     const uint32_t hi = 0x64646464u;
@@ -215,7 +203,6 @@ struct WTileB {
   // fp16(code * scale): each pair of codes under the fp16 exponent of 1024
   // reads as 1024 + code + 2^(b-1); one packed subtract makes the codes exact,
   // one packed multiply by the scale rounds each product to nearest even.
-  template <bool>
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     const uint32_t sb = scale_bits(f, s);
     const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
