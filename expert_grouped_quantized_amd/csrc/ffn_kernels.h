@@ -263,27 +263,50 @@ __device__ __forceinline__ void run_routed_tile(const FfnArgs& A, const TileJob&
 // on XCD b % 8; slot = (b / (8*NB)) * 8 + b % 8, nb = (b / 8) % NB.  So all
 // column blocks of one row tile share an XCD (and its L2 copy of the gathered
 // activation rows), and empty slots spread evenly over the XCDs.
+// Slots to tiles: routed tiles in plan order, then the shared expert's tiles;
+// slots past the plan's tiles are empty.  With SPREAD the shared tiles (which
+// re-read one small weight set from cache and mostly compute) are instead
+// spread evenly over the first L = shared + ceil(T*k / rows) slots -- a lower
+// bound on the routed tiles in use -- between routed tiles, so they run beside
+// tiles that stream their weights from HBM instead of forming the tail.  The
+// MXFP4 kernels use it (routed tiles there do no dequantization: T=4096 and
+// T=16 grouped FFN -4.6%); the int4 kernels do not (no gain, and the shared
+// outputs then leave the cache before the combine reads them: +3 us there).
+template <bool SPREAD = false>
 __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_routed,
                                            int ncols_shared, int rows_per_tile, TileJob& J) {
   const int b = blockIdx.x;
   const int slot = (b / (8 * NB)) * 8 + (b & 7);
   J.nb = (b >> 3) % NB;
-  if (slot < A.routed_slots) {
-    const int4 t = A.tiles[slot];  // one scalar load: (expert, first row, rows)
-    if (t.z == 0) return false;
-    J.shared = false;
-    J.expert = t.x;
-    J.start = t.y;
-    J.cnt = min(rows_per_tile, t.z);
-    return J.nb < ncols_routed;
+  const int ns = A.shared_slots, S = A.routed_slots + ns;
+  if (slot >= S) return false;
+  const int L = SPREAD ? min(S, ns + (A.T * A.k + rows_per_tile - 1) / rows_per_tile) : S;
+  int routed = SPREAD ? slot - ns : slot;
+  if (!SPREAD && slot >= A.routed_slots) {
+    J.shared = true;
+    J.expert = -1;
+    J.start = (slot - A.routed_slots) * rows_per_tile;
+    J.cnt = min(rows_per_tile, A.T - J.start);
+    return J.nb < ncols_shared;
   }
-  const int s = slot - A.routed_slots;
-  if (s >= A.shared_slots) return false;
-  J.shared = true;
-  J.expert = -1;
-  J.start = s * rows_per_tile;
-  J.cnt = min(rows_per_tile, A.T - J.start);
-  return J.nb < ncols_shared;
+  if (SPREAD && slot < L) {
+    const int before = (int)((int64_t)slot * ns / L);  // shared tiles in slots [0, slot)
+    if ((int)((int64_t)(slot + 1) * ns / L) > before) {
+      J.shared = true;
+      J.expert = -1;
+      J.start = before * rows_per_tile;
+      J.cnt = min(rows_per_tile, A.T - J.start);
+      return J.nb < ncols_shared;
+    }
+    routed = slot - before;
+  }
+  const int4 t = A.tiles[routed];  // one scalar load: (expert, first row, rows)
+  if (t.z == 0) return false;
+  J.shared = false;
+  J.expert = t.x;
+  J.start = t.y;
+  J.cnt = min(rows_per_tile, t.z);
+  return J.nb < ncols_routed;
 }
 
 // column blocks of a matrix with `runs` 64-row weight runs

@@ -396,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_mx_kernel(FfnArgs A
   const int nr = STAGE == 1 ? col_blocks(A.F / H_COLS_WAVE) : col_blocks(A.d / OUT_COLS_WAVE);
   const int ns = STAGE == 1 ? (A.n_shared ? col_blocks(A.Fs / H_COLS_WAVE) : 0) : nr;
   TileJob J;
-  if (!decode_job(A, max(nr, ns), nr, ns, MAXMF * 16, J)) return;
+  if (!decode_job<true>(A, max(nr, ns), nr, ns, MAXMF * 16, J)) return;
   // Routed weights stream past the caches at every call size (measured: at
   // T=4096 the few experts whose rows span two tiles re-read theirs, and
   // still the layer is faster than with cacheable loads).
