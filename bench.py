@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
-    p.add_argument("--workload", choices=("both", "prefill", "decode", "bits", "mxfp4"),
+    p.add_argument("--workload", choices=("both", "prefill", "decode", "bits", "mxfp4", "configs"),
                    default="both",
                    help="limit the run to one workload (for per-workload profiles)")
     return p.parse_args()
@@ -438,6 +438,46 @@ def run_mxfp4(args, torch, W):
     return out
 
 
+def run_configs(args, torch, W):
+    """The layer configurations measured beside the headline ones, each as
+    eager steps with the roofline its shape sits under: the bf16 layer at
+    T=512 (weight bound: every expert's bf16 weights read once), the T=4096
+    layer with bf16 routed weights (also weight bound), and T=16384 with int4
+    routed experts and Zipf-skewed routing (MFMA bound)."""
+    import dataclasses
+    cases = [("bf16_T512", W.CONFIGS["bf16_T512"], "hbm"),
+             ("bf16w_T4096", dataclasses.replace(W.CONFIGS["int4_T4096"], name="bf16w_T4096",
+                                                 expert=W.BF16), "hbm"),
+             ("zipf_T16384", W.CONFIGS["zipf_T16384"], "mfma")]
+    out = {}
+    for name, cfg, bound in cases:
+        S = Setup(cfg, cfg.T, torch)
+        steps = max(5, args.steps // (4 if cfg.T > 4096 else 1))
+        wall, layer_ms, per = time_steps(S, steps, args.warmup)
+        ms = wall * 1e3 / steps
+        counts = np.diff(S.layer.offsets.cpu().numpy())
+        act = int((counts > 0).sum())
+        A = algorithmic(cfg, cfg.T, act)
+        ffn_s = per[2] * 1e-3
+        rec = dict(T=cfg.T, routed_w=cfg.expert, shared_w=cfg.shared, bound=bound,
+                   tokens_per_s=cfg.T / (ms * 1e-3), ms_per_step=ms, layer_event_ms=layer_ms,
+                   call_ms=dict(route=per[0], permute=per[1], grouped_ffn=per[2], combine=per[3]),
+                   active_experts=act, max_over_mean_load=float(counts.max() / counts.mean()),
+                   ffn_tflops=A["ffn_flops"] / ffn_s / 1e12,
+                   ffn_mfma_frac=A["ffn_flops"] / ffn_s / 1e12 / BF16_PEAK_TFLOPS,
+                   ffn_algorithmic_bytes=A["ffn_bytes"],
+                   ffn_gbs=A["ffn_bytes"] / ffn_s / 1e9,
+                   ffn_hbm_frac=A["ffn_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS,
+                   layer_hbm_frac=A["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        out[name] = rec
+        print(f"[bench] {name}: {ms:.3f} ms/step (ffn {per[2]:.3f} ms, "
+              f"{rec['ffn_tflops']:.0f} TFLOP/s, {rec['ffn_gbs']:.0f} GB/s)", file=sys.stderr,
+              flush=True)
+        del S
+        torch.cuda.empty_cache()
+    return out
+
+
 def _r(d):
     return {k: (round(v, 4) if isinstance(v, float) else _r(v) if isinstance(v, dict) else v)
             for k, v in d.items()}
@@ -470,6 +510,16 @@ def main():
                                      "routed_w": "b-bit symmetric codes, fp16 scale per 32",
                                      "shared_w": "int8 per-row fp16 scales"},
                           "bit_widths": _r(bits)}), flush=True)
+        return
+    if args.workload == "configs":
+        cf = run_configs(args, torch, W)
+        print(json.dumps({"metric": "MoE-layer tokens/s and roofline fraction of the other layer "
+                                    "configurations (bf16 T=512, bf16 routed weights at T=4096, "
+                                    "Zipf-skewed T=16384)",
+                          "unit": "tokens/s", "n_gpus": 1, "data": "synthetic",
+                          "peaks": {"bf16_mfma_tflops": BF16_PEAK_TFLOPS,
+                                    "hbm_gbs": HBM_PEAK_GBS},
+                          "configs": _r(cf)}), flush=True)
         return
     if args.workload == "mxfp4":
         mx = run_mxfp4(args, torch, W)
