@@ -312,7 +312,7 @@ __device__ __forceinline__ bool decode_job(const FfnArgs& A, int NB, int ncols_r
 // column blocks of a matrix with `runs` 64-row weight runs
 __host__ __device__ __forceinline__ int col_blocks(int runs) { return (runs + WAVES - 1) / WAVES; }
 
-template <int RF, int SF, int STAGE, int MAXMF, int PF>
+template <int RF, int SF, int STAGE, int MAXMF, int PF, bool NT_ROUTED>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   __shared__ __attribute__((aligned(16))) Smem<MAXMF> sm;
   const int nr = STAGE == 1 ? col_blocks(A.F / H_COLS_WAVE) : col_blocks(A.d / OUT_COLS_WAVE);
@@ -322,10 +322,10 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   // int4 routed layers run gate/up on fp16 MFMA (the fp16 activation copy
   // exists); int8 shared tiles of such a layer follow; bf16 weights stay bf16
   constexpr bool X16 = x16_path(RF, MAXMF);
-  // Routed weights of a small-T call are read exactly once: stream them.  The
-  // shared expert's weights are re-read by every row tile, and a prefill
-  // expert can span two tiles: keep those cacheable.
-  constexpr bool NT_ROUTED = MAXMF <= 2, NT_SHARED = false;
+  // NT_ROUTED: routed weights streamed past the caches (non-temporal).  The
+  // shared expert's weights are re-read by every row tile: those stay
+  // cacheable.
+  constexpr bool NT_SHARED = false;
   if (J.shared)
     run_tile<SF, STAGE, MAXMF, PF, STAGE == 1 && X16 && SF == MOE_I8_ROW, NT_SHARED>(A, J, sm);
   else
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
 // with at most 16 or 32 tokens has at most that many rows per expert (a token
 // picks an expert once), so it runs a kernel built for 1 or 2 row fragments
 // with a deeper weight prefetch; shared-expert tiles then hold 16 or 32 tokens.
-template <int RF, int SF, int MAXMF, int PF>
+template <int RF, int SF, int MAXMF, int PF, bool NT_ROUTED>
 static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
   FfnArgs a = a0;
   a.shared_slots = a.n_shared ? (a.T + MAXMF * 16 - 1) / (MAXMF * 16) : 0;
@@ -347,18 +347,27 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
     hipError_t e = launch_x_to_f16(a, s);
     if (e != hipSuccess) return e;
   }
-  ffn_kernel<RF, SF, 1, MAXMF, PF><<<slots * nb1, WAVES * 64, 0, s>>>(a);
+  ffn_kernel<RF, SF, 1, MAXMF, PF, NT_ROUTED><<<slots * nb1, WAVES * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ffn_kernel<RF, SF, 2, MAXMF, PF><<<slots * nb2, WAVES * 64, 0, s>>>(a);
+  ffn_kernel<RF, SF, 2, MAXMF, PF, NT_ROUTED><<<slots * nb2, WAVES * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// Routed weights are streamed past the caches when the call averages at most
+// one row tile per expert (every small-T call; T=4096 at k=10 of 512): each
+// expert's weights are then read about once, and keeping them out of L2 and
+// the MALL leaves room for the gathered activation rows and for the fp32
+// outputs the combine reads next (T=4096: combine 82 -> 73 us; bf16 weights
+// at T=512: grouped FFN -7%).  With more rows per expert its tiles re-read
+// its weights, which then stay cacheable (T=16384 streamed: +2%).
 template <int RF, int SF>
 static hipError_t launch_pair(const FfnArgs& a, hipStream_t s) {
-  if (a.T <= 16) return launch_stages<RF, SF, 1, LEAD_I4>(a, s);
-  if (a.T <= 32) return launch_stages<RF, SF, 2, LEAD_I4>(a, s);
-  return launch_stages<RF, SF, BM / 16, LEAD_I4>(a, s);
+  if (a.T <= 16) return launch_stages<RF, SF, 1, LEAD_I4, true>(a, s);
+  if (a.T <= 32) return launch_stages<RF, SF, 2, LEAD_I4, true>(a, s);
+  if ((int64_t)a.T * a.k <= (int64_t)a.E * BM)
+    return launch_stages<RF, SF, BM / 16, LEAD_I4, true>(a, s);
+  return launch_stages<RF, SF, BM / 16, LEAD_I4, false>(a, s);
 }
 
 }  // namespace moe
