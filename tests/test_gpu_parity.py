@@ -340,17 +340,36 @@ def test_int4_decode_full(T):
     _say(f"[ok] int4_decode T={T}", r, "active experts", int((np.diff(out['offsets']) > 0).sum()))
 
 
-def _mx_variant(name, T=None):
-    """The named workload with MXFP4 W4A4 routed experts (same draws)."""
+def _variant(name, expert, T=None):
+    """The named workload with another routed-expert format (same draws)."""
     from dataclasses import replace
-    key = (name + "/mxfp4", T)
+    key = (f"{name}/{expert}", T)
     if key not in _CACHE:
-        cfg = replace(W.CONFIGS[name], name=name + "_mxfp4", expert=W.MXFP4)
+        cfg = replace(W.CONFIGS[name], name=f"{name}_{expert}", expert=expert)
         _say(f"[gen] {cfg.name} T={T or cfg.T}")
         inputs = W.generate(cfg, T=T)
         _CACHE.clear()
         _CACHE[key] = (cfg, inputs, GpuLayer(cfg, inputs))
     return _CACHE[key]
+
+
+def _mx_variant(name, T=None):
+    """The named workload with MXFP4 W4A4 routed experts (same draws)."""
+    return _variant(name, W.MXFP4, T)
+
+
+def test_bf16_weights_T4096_sampled():
+    """The T=4096 layer with bf16 routed weights (the weight-bound prefill
+    point): 96-row tiles on bf16 MFMA with no dequantization, weights streamed
+    past the caches at a two-chunk lead."""
+    cfg, inp, g = _variant("int4_T4096", W.BF16)
+    _say("[run] bf16 weights T=4096")
+    out = g.run(inp["x"])
+    tok = _sample(cfg.T, 24, 7)
+    ids_o, w_o = check_route(cfg, inp, out, tokens=tok)
+    check_plan(cfg, out)
+    r = check_values(cfg, inp, out, w_o, tokens=tok)
+    _say("[ok] bf16 weights T=4096", r)
 
 
 def test_mxfp4_T4096_sampled():
