@@ -8,7 +8,11 @@ namespace moe {
 // Activations of an int4 layer as fp16: each token row is scaled by 2^-e so
 // its largest magnitude lies in [2^14, 2^15) -- every bf16 value of the row is
 // then exact in fp16 unless it is 2^-28 below the row's largest -- and 2^e is
-// kept for the gate/up epilogue.  One wave per row.
+// kept for the gate/up epilogue.  One wave per row; each lane reads its
+// pieces XB at a time with no condition on the loads (indices past the row
+// re-read its last piece: harmless for the maximum, and never stored), so a
+// batch is in flight at once instead of one load per round trip.
+constexpr int XB = 8;  // 16-byte pieces per lane per batch (d <= 4096 in one)
 __global__ __launch_bounds__(256) void x_to_f16_kernel(int T, int d, const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ x16,
                                                        float* __restrict__ xscale) {
@@ -18,13 +22,17 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(int T, int d, const uint1
   const u32x4_t* src = (const u32x4_t*)(x + (size_t)t * d);
   const int pieces = d / 8;
   uint32_t mx = 0;  // largest |x| as float bits (non-negative floats order as integers)
-  for (int p = lane; p < pieces; p += 64) {
-    const u32x4_t v = src[p];
+  for (int p0 = 0; p0 < pieces; p0 += 64 * XB) {
+    u32x4_t v[XB];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint32_t a = (v[j] << 16) & 0x7fffffffu, b = v[j] & 0x7fff0000u;
-      mx = max(mx, max(a, b));
-    }
+    for (int j = 0; j < XB; j++) v[j] = src[min(p0 + 64 * j + lane, pieces - 1)];
+#pragma unroll
+    for (int j = 0; j < XB; j++)
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const uint32_t a = (v[j][w] << 16) & 0x7fffffffu, b = v[j][w] & 0x7fff0000u;
+        mx = max(mx, max(a, b));
+      }
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
@@ -37,15 +45,21 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(int T, int d, const uint1
   const float down = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
   if (lane == 0) xscale[t] = __uint_as_float((uint32_t)(127 + e) << 23);
   u32x4_t* dst = (u32x4_t*)(x16 + (size_t)t * d);
-  for (int p = lane; p < pieces; p += 64) {
-    const u32x4_t v = src[p];
-    u32x4_t o;
+  for (int p0 = 0; p0 < pieces; p0 += 64 * XB) {
+    u32x4_t v[XB];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      f16x2_t h = {(_Float16)(bf16_lo(v[j]) * down), (_Float16)(bf16_hi(v[j]) * down)};
-      o[j] = __builtin_bit_cast(uint32_t, h);
+    for (int j = 0; j < XB; j++) v[j] = src[min(p0 + 64 * j + lane, pieces - 1)];
+#pragma unroll
+    for (int j = 0; j < XB; j++) {
+      const int p = p0 + 64 * j + lane;
+      u32x4_t o;
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        f16x2_t h = {(_Float16)(bf16_lo(v[j][w]) * down), (_Float16)(bf16_hi(v[j][w]) * down)};
+        o[w] = __builtin_bit_cast(uint32_t, h);
+      }
+      if (p < pieces) dst[p] = o;
     }
-    dst[p] = o;
   }
 }
 

@@ -88,10 +88,21 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     // the parts are then added through LDS (integer sums: order-free)
     const int r = PLAN_THREADS / E, e = tid % E, part = tid / E;
     if (part < r) {
-      for (int c = part; c < n_chunks; c += r) {
-        const int v = counts[(size_t)c * E + e];
-        if (c < chunk) before += v;
-        total += v;
+      // eight chunks' counts a batch, loaded with no condition (indices past
+      // the last chunk re-read it and are not added) so they are in flight
+      // together
+      for (int c0 = part; c0 < n_chunks; c0 += 8 * r) {
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = counts[(size_t)min(c0 + j * r, n_chunks - 1) * E + e];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const int c = c0 + j * r;
+          if (c < n_chunks) {
+            if (c < chunk) before += v[j];
+            total += v[j];
+          }
+        }
       }
     }
     hist[tid] = total;

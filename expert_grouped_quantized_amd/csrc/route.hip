@@ -289,12 +289,16 @@ __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // The PL loads carry no condition (slots past E re-read the row's last
+  // logit), so they issue back to back under one wait; a per-slot guarded
+  // load would wait for each in turn.
   uint32_t key[PL];
+  float lv[PL];
+  const float* row = logits + (size_t)t * E;
 #pragma unroll
-  for (int j = 0; j < PL; j++) {
-    const int e = j * 64 + lane;
-    key[j] = e < E ? order_key(logits[(size_t)t * E + e]) : 0u;
-  }
+  for (int j = 0; j < PL; j++) lv[j] = row[min(j * 64 + lane, E - 1)];
+#pragma unroll
+  for (int j = 0; j < PL; j++) key[j] = j * 64 + lane < E ? order_key(lv[j]) : 0u;
   auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
   auto umin = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
   uint32_t bk = 0;
