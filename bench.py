@@ -486,8 +486,8 @@ def _r(d):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
-              "multi-GPU path.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs the "
+              "layer on one GPU and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads as W
