@@ -338,10 +338,10 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
     run_routed_tile<RF, STAGE, MAXMF, PF, STAGE == 1 && X16, NT_ROUTED>(A, J, sm);
 }
 
-// Row tiles come from the route plan (at most BM = 96 rows each).  A call
-// with at most 16 or 32 tokens has at most that many rows per expert (a token
-// picks an expert once), so it runs a kernel built for 1 or 2 row fragments
-// with a deeper weight prefetch; shared-expert tiles then hold 16 or 32 tokens.
+// Row tiles come from the route plan, cut at tile_rows(T) rows: a call with
+// at most 16 or 32 tokens runs a kernel built for 1 or 2 row fragments with a
+// deeper weight prefetch (shared-expert tiles then hold 16 or 32 tokens), a
+// larger call 96-row tiles.
 template <int RF, int SF, int MAXMF, int PF, bool NT_ROUTED>
 static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
   FfnArgs a = a0;
@@ -369,6 +369,8 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
 // its weights, which then stay cacheable (T=16384 streamed: +2%).
 template <int RF, int SF>
 static hipError_t launch_pair(const FfnArgs& a, hipStream_t s) {
+  static_assert(tile_rows(16) == 16 && tile_rows(32) == 32 && tile_rows(33) == BM,
+                "kernel choice follows the route plan's tile rows");
   if (a.T <= 16) return launch_stages<RF, SF, 1, LEAD_I4, true>(a, s);
   if (a.T <= 32) return launch_stages<RF, SF, 2, LEAD_I4, true>(a, s);
   if ((int64_t)a.T * a.k <= (int64_t)a.E * BM)

@@ -43,6 +43,13 @@ constexpr int KC_MX = 128;
 constexpr int TILE_BYTES_MX4 = 64 * 128 / 2 + 64 * 4;  // 4352
 constexpr int LEAD_MX = 2;
 
+// Rows of a routed row tile in a call of T tokens.  moe_permute cuts every
+// expert's group into tiles of this many rows and moe_grouped_ffn launches the
+// kernels built for that tile: one or two 16-row fragments for calls of at most
+// 16 or 32 tokens, BM rows above.  A group can outgrow T (a caller's ids may
+// name one expert twice for a token), so the cut must not assume it cannot.
+__host__ __device__ constexpr int tile_rows(int64_t T) { return T <= 16 ? 16 : T <= 32 ? 32 : BM; }
+
 // ---- route plan ----------------------------------------------------------
 constexpr int PLAN_CHUNK = 1024;   // assignments per block of the plan kernels
 constexpr int PLAN_THREADS = 1024; // 16 waves
@@ -116,7 +123,8 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   WsLayout L{};
   int64_t n = T * k;
   L.n_chunks = (int)((n + PLAN_CHUNK - 1) / PLAN_CHUNK);
-  int64_t bound = (n + BM - 1) / BM + (n < D.n_experts ? n : D.n_experts);
+  const int64_t R = tile_rows(T);
+  int64_t bound = (n + R - 1) / R + (n < D.n_experts ? n : D.n_experts);
   L.routed_slots = (int)(bound < n ? bound : n);
   size_t elem = D.act == MOE_F32 ? 4 : 2;
   size_t off = 0;
@@ -140,8 +148,9 @@ hipError_t launch_router_f32(int T, int d, int E, const float* x, const float* w
                              const float* bias, float* logits, hipStream_t s);
 hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w,
                        hipStream_t s);
-hipError_t launch_plan(int n, int E, const int32_t* ids, int32_t* offsets, int32_t* perm,
-                       int32_t* inv_perm, void* ws, const WsLayout& L, hipStream_t s);
+hipError_t launch_plan(int n, int E, int rows, const int32_t* ids, int32_t* offsets,
+                       int32_t* perm, int32_t* inv_perm, void* ws, const WsLayout& L,
+                       hipStream_t s);
 
 struct FfnArgs {
   int T, k, d, E, F, Fs, n_shared;

@@ -1,4 +1,5 @@
-// permute.hip -- the deterministic expert-major route plan
+// permute.hip -- the route plan: every assignment ordered by expert, the same
+// order on every run
 // ("Qwen3.8-Flash-Next-Dual-GPU" README, section "Dedicated prefill lane",
 // step 1; TandemLLM docs 17.4: a chunk sorts its (row, expert) pairs by expert).
 //
@@ -65,7 +66,7 @@ template <bool SINGLE>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     int n, int E, int n_chunks, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv_perm, int slots, int4* __restrict__ tiles) {
+    int32_t* __restrict__ inv_perm, int rows, int slots, int4* __restrict__ tiles) {
   __shared__ int run[MAX_EXPERTS];
   __shared__ int hist[MAX_EXPERTS];
   __shared__ __attribute__((aligned(16))) uint8_t wcnt[PLAN_WAVES][MAX_EXPERTS];
@@ -122,13 +123,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
   if (chunk == 0) {
     if (tid < E) offsets[tid] = off;
     if (tid == 0) offsets[E] = n;
-    // 3) row tiles of the grouped GEMMs: expert e owns ceil(total/BM) tiles,
-    //    each stored resolved (expert, first row, rows) so a GEMM block finds
-    //    its rows with one load; the slots past the plan's tiles hold 0 rows
-    const int nt = tid < E ? (total + BM - 1) / BM : 0;
+    // 3) row tiles of the grouped GEMMs: expert e owns ceil(total/rows)
+    //    tiles, each stored resolved (expert, first row, rows) so a GEMM block
+    //    finds its rows with one load; the slots past the plan's tiles hold 0
+    //    rows
+    const int nt = tid < E ? (total + rows - 1) / rows : 0;
     const int tstart = block_exclusive_scan(nt, wsum, &total_all);
     for (int j = 0; j < nt; j++)
-      tiles[tstart + j] = make_int4(tid, off + j * BM, min(BM, total - j * BM), 0);
+      tiles[tstart + j] = make_int4(tid, off + j * rows, min(rows, total - j * rows), 0);
     for (int j = total_all + tid; j < slots; j += PLAN_THREADS) tiles[j] = make_int4(0, 0, 0, 0);
   }
   __syncthreads();
@@ -173,20 +175,21 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
   }
 }
 
-hipError_t launch_plan(int n, int E, const int32_t* ids, int32_t* offsets, int32_t* perm,
-                       int32_t* inv_perm, void* ws, const WsLayout& L, hipStream_t s) {
+hipError_t launch_plan(int n, int E, int rows, const int32_t* ids, int32_t* offsets,
+                       int32_t* perm, int32_t* inv_perm, void* ws, const WsLayout& L,
+                       hipStream_t s) {
   uint8_t* w = (uint8_t*)ws;
   int32_t* counts = (int32_t*)(w + L.counts);
   int4* tiles = (int4*)(w + L.tiles);
   if (L.n_chunks == 1) {
     plan_scatter_kernel<true><<<1, PLAN_THREADS, 0, s>>>(n, E, 1, ids, counts, offsets, perm,
-                                                         inv_perm, L.routed_slots, tiles);
+                                                         inv_perm, rows, L.routed_slots, tiles);
   } else {
     plan_count_kernel<<<L.n_chunks, PLAN_THREADS, 0, s>>>(n, E, ids, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     plan_scatter_kernel<false><<<L.n_chunks, PLAN_THREADS, 0, s>>>(
-        n, E, L.n_chunks, ids, counts, offsets, perm, inv_perm, L.routed_slots, tiles);
+        n, E, L.n_chunks, ids, counts, offsets, perm, inv_perm, rows, L.routed_slots, tiles);
   }
   return hipGetLastError();
 }
