@@ -1,5 +1,6 @@
 // abi.cpp -- the C ABI of include/moe.h: argument checks (host only, before
 // anything is enqueued), the blob packer, workspace sizing and launch dispatch.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -127,6 +128,20 @@ inline uint16_t i4_scale(const MatIO& m, int64_t r, int64_t k) {
   return ((const uint16_t*)m.s)[r * (m.K / 32) + k / 32];
 }
 
+// Outcome of packing one tile or expert.
+enum PackResult { PK_OK = 0, PK_CODE = 1, PK_SCALE = 2 };
+
+// An fp16 scale the kernels can use: finite, and for group-32 codes with
+// largest magnitude qmax (0 for per-row int8 scales), |s| * qmax must stay
+// below 65520 so that fp16(code * s) -- the gate/up products run on fp16
+// weights -- never rounds to infinity.
+inline bool f16_scale_ok(uint16_t bits, int qmax) {
+  if ((bits & 0x7c00u) == 0x7c00u) return false;  // inf or NaN
+  const int e = (bits >> 10) & 31, m = bits & 1023;
+  const double mag = e ? ldexp(1024 + m, e - 25) : ldexp(m, -24);
+  return mag * qmax < 65520.0;
+}
+
 // One 64-row x 64-K wave tile, laid out for the 16x16x32 MFMA.  Fragment f
 // (0..3) takes 16 rows from matrix m[f], rows row_of(f, c) for c = 0..15;
 // K step s (0..1) covers 32 K.  Lane l of the consuming wave holds row
@@ -145,7 +160,7 @@ struct OutIO {  // canonical outputs of unpacking
 // stream (code + 2^(b-1) at bit (2f + s) 8b + i b for element i), then the
 // fp16 group scales [row c][f][s] at 512 b + c*16.
 template <typename RowOf>
-bool pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
+int pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   const int b = ig32_bits(m[0]->fmt), lim = (1 << (b - 1)) - 1;
   for (int lane = 0; lane < 64; lane++) {
     uint32_t w[17] = {0};  // one spare dword: a field may reach past the last
@@ -156,7 +171,7 @@ bool pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* 
         const int64_t k0 = kc * KC + s * 32 + 8 * (lane >> 4);
         for (int i = 0; i < 8; i++) {
           const int c = ((const int8_t*)M.q)[r * M.K + k0 + i];
-          if (c < -lim || c > lim) return false;
+          if (c < -lim || c > lim) return PK_CODE;
           const uint64_t u = (uint64_t)(c + (1 << (b - 1)));
           const int bit = (2 * f + s) * 8 * b + i * b;
           const uint64_t cur = ((uint64_t)w[(bit >> 5) + 1] << 32) | w[bit >> 5];
@@ -171,9 +186,12 @@ bool pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* 
   for (int c = 0; c < 16; c++) {
     uint16_t* o = (uint16_t*)(dst + 512 * b + c * 16);
     for (int f = 0; f < 4; f++)
-      for (int s = 0; s < 2; s++) o[f * 2 + s] = i4_scale(*m[f], row_of(f, c), kc * KC + s * 32);
+      for (int s = 0; s < 2; s++) {
+        o[f * 2 + s] = i4_scale(*m[f], row_of(f, c), kc * KC + s * 32);
+        if (!f16_scale_ok(o[f * 2 + s], lim)) return PK_SCALE;
+      }
   }
-  return true;
+  return PK_OK;
 }
 
 // MXFP4 tile (64 rows x 128 K, for the scaled FP4 MFMA 16x16x128): lane l of
@@ -183,7 +201,7 @@ bool pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* 
 // f*1024 + l*16; lane l's four E8M0 scales (byte f = fragment f) at
 // 4096 + l*4.  Returns false on a NaN (255) scale.
 template <typename RowOf>
-bool pack_tile_mx(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
+int pack_tile_mx(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   for (int lane = 0; lane < 64; lane++) {
     const int kb = lane >> 4;
     for (int f = 0; f < 4; f++) {
@@ -191,15 +209,15 @@ bool pack_tile_mx(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* ds
       const int64_t r = row_of(f, lane & 15);
       memcpy(dst + f * 1024 + lane * 16, M.q + r * (M.K / 2) + kc * (KC_MX / 2) + kb * 16, 16);
       const uint8_t sc = M.s[r * (M.K / 32) + kc * 4 + kb];
-      if (sc == 255) return false;
+      if (sc == 255) return PK_SCALE;
       dst[4096 + lane * 4 + f] = sc;
     }
   }
-  return true;
+  return PK_OK;
 }
 
 template <typename RowOf>
-bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
+int pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   const int fmt = m[0]->fmt;
   if (fmt == MOE_MXFP4) return pack_tile_mx(m, row_of, kc, dst);
   if (fmt != MOE_I4_G32 && ig32_bits(fmt) != 0) return pack_tile_ig32(m, row_of, kc, dst);
@@ -215,7 +233,7 @@ bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) 
           uint32_t word = 0;  // element 2j in nibble j, element 2j+1 in nibble j+4
           for (int i = 0; i < 8; i++) {
             const int c = i4_code(M, r, k0 + i);
-            if (c < -7) return false;
+            if (c < -7) return PK_CODE;
             word |= (uint32_t)(c + 8) << (4 * i4_nibble(i));
           }
           memcpy(dst + ((size_t)(f >> 1) * 64 + lane) * 16 + ((f & 1) * 2 + s) * 4, &word, 4);
@@ -229,10 +247,13 @@ bool pack_tile(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) 
     for (int c = 0; c < 16; c++) {
       uint16_t* o = (uint16_t*)(dst + 2048 + c * 16);
       for (int f = 0; f < 4; f++)
-        for (int s = 0; s < 2; s++) o[f * 2 + s] = i4_scale(*m[f], row_of(f, c), kc * KC + s * 32);
+        for (int s = 0; s < 2; s++) {
+          o[f * 2 + s] = i4_scale(*m[f], row_of(f, c), kc * KC + s * 32);
+          if (!f16_scale_ok(o[f * 2 + s], 7)) return PK_SCALE;
+        }
     }
   }
-  return true;
+  return PK_OK;
 }
 
 template <typename RowOf>
@@ -335,9 +356,10 @@ struct ExpertIO {  // canonical pointers of one expert (gate, up, down)
   const uint8_t *g, *gs, *u, *us, *dn, *ds;
 };
 
-// Pack (or, with unpack = true, unpack) one expert.  Returns false on a code
-// outside its format's symmetric range.
-bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool unpack) {
+// Pack (or, with unpack = true, unpack) one expert.  Returns PK_CODE on a code
+// outside its format's symmetric range, PK_SCALE on a scale the kernels cannot
+// use (f16_scale_ok; an MXFP4 scale byte of 255).
+int pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool unpack) {
   const size_t w1b = w1_bytes(fmt, d, F);
   if (fmt == MOE_F32) {
     if (!unpack) {
@@ -349,7 +371,7 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
       memcpy((void*)io.u, blob + F * d * 4, F * d * 4);
       memcpy((void*)io.dn, blob + w1b, d * F * 4);
     }
-    return true;
+    return PK_OK;
   }
   const size_t tb = tile_bytes(fmt);
   const int64_t nk1 = d / kc_of(fmt), nk2 = F / kc_of(fmt);
@@ -365,7 +387,7 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
     for (int64_t kc = 0; kc < nk1; kc++) {
       uint8_t* t = blob + ((size_t)j * nk1 + kc) * tb;
       if (!unpack) {
-        if (!pack_tile(m1, row_of, kc, t)) return false;
+        if (const int r = pack_tile(m1, row_of, kc, t)) return r;
       } else {
         unpack_tile(m1, o1, row_of, kc, t);
       }
@@ -382,7 +404,7 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
     for (int64_t kc = 0; kc < nk2; kc++) {
       uint8_t* t = w2 + ((size_t)j * nk2 + kc) * tb;
       if (!unpack) {
-        if (!pack_tile(m2, row_of, kc, t)) return false;
+        if (const int r = pack_tile(m2, row_of, kc, t)) return r;
       } else {
         unpack_tile(m2, o2, row_of, kc, t);
       }
@@ -395,13 +417,19 @@ bool pack_expert(int fmt, int64_t d, int64_t F, ExpertIO io, uint8_t* blob, bool
       memcpy(s1, io.gs, F * 2);
       memcpy(s1 + F * 2, io.us, F * 2);
       memcpy(s2, io.ds, d * 2);
+      const uint16_t* rs[3] = {(const uint16_t*)io.gs, (const uint16_t*)io.us,
+                               (const uint16_t*)io.ds};
+      const int64_t nrs[3] = {F, F, d};
+      for (int j = 0; j < 3; j++)
+        for (int64_t r = 0; r < nrs[j]; r++)
+          if (!f16_scale_ok(rs[j][r], 0)) return PK_SCALE;
     } else {
       memcpy((void*)io.gs, s1, F * 2);
       memcpy((void*)io.us, s1 + F * 2, F * 2);
       memcpy((void*)io.ds, s2, d * 2);
     }
   }
-  return true;
+  return PK_OK;
 }
 
 moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, const void* gs,
@@ -429,7 +457,7 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
       ExpertIO io{(const uint8_t*)gate + e * gq, gs ? (const uint8_t*)gs + e * gsb : nullptr,
                   (const uint8_t*)up + e * gq,   us ? (const uint8_t*)us + e * gsb : nullptr,
                   (const uint8_t*)down + e * dq, ds ? (const uint8_t*)ds + e * dsb : nullptr};
-      if (!pack_expert(fmt, d, F, io, (uint8_t*)blob + e * eb, unpack)) bad[e] = 1;
+      bad[e] = (char)pack_expert(fmt, d, F, io, (uint8_t*)blob + e * eb, unpack);
     }
   };
   const int nt = (int)std::max<int64_t>(1, std::min<int64_t>(n, std::max(1u, std::thread::hardware_concurrency())));
@@ -441,9 +469,19 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
       if (fmt == MOE_MXFP4)
         return fail(MOE_EINVAL, "expert %lld holds an MXFP4 scale byte of 255 (NaN)",
                     (long long)e);
-      const int b = ig32_bits(fmt);
-      return fail(MOE_EINVAL, "expert %lld holds a code outside [%d, %d]", (long long)e,
-                  -((1 << (b - 1)) - 1), (1 << (b - 1)) - 1);
+      const int b = fmt == MOE_I8_ROW ? 8 : ig32_bits(fmt);
+      const int qmax = (1 << (b - 1)) - 1;
+      if (bad[e] == PK_SCALE) {
+        if (fmt == MOE_I8_ROW)
+          return fail(MOE_EINVAL, "expert %lld holds a row scale that is not finite",
+                      (long long)e);
+        return fail(MOE_EINVAL,
+                    "expert %lld holds a group scale that is not finite or whose %d-fold "
+                    "overflows fp16 (|scale| * %d must stay below 65520)",
+                    (long long)e, qmax, qmax);
+      }
+      return fail(MOE_EINVAL, "expert %lld holds a code outside [%d, %d]", (long long)e, -qmax,
+                  qmax);
     }
   return ok();
 }
@@ -548,8 +586,8 @@ moe_status moe_permute(const moe_desc* D, int32_t T, int32_t k, const int32_t* t
   if (ws_bytes < L.total)
     return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if (T == 0) return ok();
-  return device_result(launch_plan(T * k, D->n_experts, topk_ids, offsets, perm, inv_perm,
-                                   workspace, L, (hipStream_t)stream),
+  return device_result(launch_plan(T * k, D->n_experts, tile_rows(T), topk_ids, offsets, perm,
+                                   inv_perm, workspace, L, (hipStream_t)stream),
                        "route-plan launch");
 }
 

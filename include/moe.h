@@ -4,12 +4,15 @@
  * The layer (pages on serving Qwen3.8-Flash-Next):
  *   - TandemLLM docs, chapter 17 "Qwen3.8-Flash-Next", Table 17.1: 512 routed
  *     experts a layer; every token runs 10 of them plus 1 shared expert.
- *   - "Qwen3.8-Flash-Next-Dual-GPU" README, section "Dedicated prefill lane":
- *     build a deterministic expert-major route plan on the GPU (moe_permute),
- *     run the matrix work expert by expert on 4/8-bit weights with 16-bit
- *     activations, fold the router weights into the intermediate activation,
- *     write one FP32 output per assignment (moe_grouped_ffn), and reduce each
- *     token's routes in a fixed order without atomics (moe_combine).
+ *   - "Qwen3.8-Flash-Next-Dual-GPU" README, section "Dedicated prefill lane"
+ *     (its numbered list): the grouped lane this library implements.
+ *     moe_permute orders every (token, slot) assignment by expert on the GPU,
+ *     identically on every run; moe_grouped_ffn runs each expert's SwiGLU
+ *     once over all of its rows (quantized weights, 16-bit activations),
+ *     scales the intermediate by the token's routing weight before the down
+ *     projection, and keeps each assignment's result as its own fp32 row;
+ *     moe_combine adds a token's rows in slot order, so nothing accumulates
+ *     through atomics.
  *   - same README, section "Independent decode lane": the 512-expert router
  *     uses a deterministic stable top-k (moe_route).
  *   - same README, "Model artifact and memory placement" table: routed experts
@@ -146,7 +149,12 @@ moe_status moe_blob_bytes(const moe_desc* desc, int32_t kind, size_t* bytes);
  * inputs hold n_experts experts stacked; for SHARED one expert.
  * MOE_I4_G32 codes must lie in [-7, 7] (symmetric); an 8 (-8) code returns
  * MOE_EINVAL, as does a b-bit code outside [-(2^(b-1) - 1), 2^(b-1) - 1] and
- * an MXFP4 scale byte of 255.
+ * an MXFP4 scale byte of 255.  fp16 scales must be finite; a group scale of
+ * the int4 or b-bit formats must also keep its largest product finite in
+ * fp16, |scale| * (2^(b-1) - 1) < 65520 (|scale| <= 9352 for int4), because
+ * the gate/up products take fp16(code * scale) as their weights; any other
+ * scale returns MOE_EINVAL.  Scales below fp16's normal range are fine: a
+ * code times such a scale is exact or rounded at fp16 precision.
  * Host only.                                                                */
 moe_status moe_pack_experts(const moe_desc* desc, int32_t kind, const void* gate,
                             const void* gate_scales, const void* up, const void* up_scales,
@@ -184,7 +192,8 @@ moe_status moe_route(const moe_desc* desc, int32_t T, int32_t k, const void* hid
 moe_status moe_route_from_logits(const moe_desc* desc, int32_t T, int32_t k, const float* logits,
                                  int32_t* topk_ids, float* topk_w, void* stream);
 
-/* Deterministic expert-major route plan ("Dedicated prefill lane", step 1).
+/* Route plan ("Dedicated prefill lane", step 1): the assignments ordered by
+ * expert, the same order on every run.
  *   topk_ids  [T*k] int32, flat index f = t*k + s, values in [0, E)
  *   offsets   [E+1] int32 out: offsets[e] = #{f : ids[f] < e}; offsets[E] = T*k
  *   perm      [T*k] int32 out: the f of expert e, ascending, at

@@ -172,6 +172,30 @@ def test_pack_unpack_roundtrip(act, fmt, kind):
     assert blob.nbytes == M.moe_blob_bytes(desc, kind)
 
 
+@pytest.mark.parametrize("d,F", [(16384, 256), (256, 16384)])
+@pytest.mark.parametrize("fmt,kind", [("bf16", 0), ("i4g32", 0), ("i8row", 1), ("mxfp4", 0)]
+                         + [(f, 0) for f in W.IG32.values()])
+def test_pack_unpack_roundtrip_max_widths(fmt, kind, d, F):
+    """Round trip at the largest widths the ABI takes (d or ffn = 16384): the
+    tile and bit-stream offsets of the packer span the whole index range."""
+    rng = np.random.default_rng(abs(hash((fmt, kind, d))) % 2**32)
+    desc = M.make_desc(d, 1, F, 1, F, act="bf16", expert_w=fmt if kind == 0 else "bf16",
+                       shared_w=fmt if kind == 1 else "bf16")
+    g, gs = _rand_expert(fmt, F, d, 1, rng)
+    u, us = _rand_expert(fmt, F, d, 1, rng)
+    dn, ds = _rand_expert(fmt, d, F, 1, rng)
+    if kind == 1:
+        g, u, dn = g[0], u[0], dn[0]
+        gs, us, ds = (None if x is None else x[0] for x in (gs, us, ds))
+    blob = np.empty(M.moe_blob_bytes(desc, kind), np.uint8)
+    M.moe_pack_experts(desc, kind, g, gs, u, us, dn, ds, blob)
+    outs = [np.zeros_like(a) if a is not None else None for a in (g, gs, u, us, dn, ds)]
+    M.moe_unpack_experts(desc, kind, blob, *outs)
+    for a, b in zip((g, gs, u, us, dn, ds), outs):
+        if a is not None:
+            assert np.array_equal(a, b)
+
+
 def test_pack_rejects_int4_minus_eight():
     desc = M.make_desc(256, 1, 256, 0, 0, act="bf16", expert_w="i4g32")
     q = np.zeros((1, 256, 256), np.int8)
@@ -243,3 +267,71 @@ def test_mxfp4_blob_bytes_rejections_and_width():
     with pytest.raises(M.MoeError) as ei:
         M.moe_pack_experts(desc, 0, q, s, q, s, q, bad, blob)
     assert ei.value.status == M.MOE_EINVAL and "expert 1" in str(ei.value) and "255" in str(ei.value)
+
+
+def _i4_expert_arrays(desc, scale_bits):
+    """One int4 expert (d=256, F=256) with every code 7 and every group scale
+    set to the fp16 bit pattern scale_bits."""
+    d, F = desc.d, desc.ffn
+    q = np.full((desc.n_experts, F, d // 2), 0x77, np.uint8)
+    qd = np.full((desc.n_experts, d, F // 2), 0x77, np.uint8)
+    sg = np.full((desc.n_experts, F, d // 32), scale_bits, np.uint16)
+    sd = np.full((desc.n_experts, d, F // 32), scale_bits, np.uint16)
+    return q, sg, qd, sd
+
+
+@pytest.mark.parametrize("scale,ok", [(9352.0, True), (9360.0, False), (65504.0, False),
+                                      (2.0 ** -24, True), (2.0 ** -16, True), (1.0, True),
+                                      (np.inf, False), (np.nan, False), (-9352.0, True),
+                                      (-9360.0, False)])
+def test_pack_checks_int4_group_scales(scale, ok):
+    """A group scale must be finite and keep 7 * scale finite in fp16 (the
+    gate/up products take fp16(code * scale) as their weights)."""
+    desc = _desc(d=256, ffn=256, n_experts=2, n_shared=0, shared_ffn=0)
+    bits = int(np.array([scale], np.float16).view(np.uint16)[0])
+    q, sg, qd, sd = _i4_expert_arrays(desc, bits)
+    blob = np.empty(M.moe_blob_bytes(desc, 0), np.uint8)
+    if ok:
+        M.moe_pack_experts(desc, 0, q, sg, q, sg, qd, sd, blob)
+    else:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_pack_experts(desc, 0, q, sg, q, sg, qd, sd, blob)
+        assert ei.value.status == M.MOE_EINVAL
+        assert "group scale" in str(ei.value)
+
+
+@pytest.mark.parametrize("b,scale,ok", [(8, 515.5, True), (8, 516.0, False), (2, 65504.0, True),
+                                        (2, np.inf, False), (5, 4364.0, True),
+                                        (5, 4368.0, False)])
+def test_pack_checks_bbit_group_scales(b, scale, ok):
+    desc = _desc(d=256, ffn=256, n_experts=1, n_shared=0, shared_ffn=0, expert_w=W.IG32[b])
+    d, F = 256, 256
+    bits = int(np.array([scale], np.float16).view(np.uint16)[0])
+    q = np.ones((1, F, d), np.int8)
+    qd = np.ones((1, d, F), np.int8)
+    sg = np.full((1, F, d // 32), bits, np.uint16)
+    sd = np.full((1, d, F // 32), bits, np.uint16)
+    blob = np.empty(M.moe_blob_bytes(desc, 0), np.uint8)
+    if ok:
+        M.moe_pack_experts(desc, 0, q, sg, q, sg, qd, sd, blob)
+    else:
+        with pytest.raises(M.MoeError, match="group scale"):
+            M.moe_pack_experts(desc, 0, q, sg, q, sg, qd, sd, blob)
+
+
+@pytest.mark.parametrize("scale,ok", [(65504.0, True), (np.inf, False), (np.nan, False)])
+def test_pack_checks_int8_row_scales(scale, ok):
+    desc = _desc(d=256, ffn=256, n_experts=1, n_shared=1, shared_ffn=256)
+    d, Fs = 256, 256
+    bits = int(np.array([scale], np.float16).view(np.uint16)[0])
+    q = np.ones((Fs, d), np.int8)
+    qd = np.ones((d, Fs), np.int8)
+    s1 = np.full(Fs, 0x3c00, np.uint16)
+    s1[17] = bits
+    sd = np.full(d, 0x3c00, np.uint16)
+    blob = np.empty(M.moe_blob_bytes(desc, 1), np.uint8)
+    if ok:
+        M.moe_pack_experts(desc, 1, q, s1, q, s1, qd, sd, blob)
+    else:
+        with pytest.raises(M.MoeError, match="row scale"):
+            M.moe_pack_experts(desc, 1, q, s1, q, s1, qd, sd, blob)
