@@ -45,11 +45,31 @@ class GpuLayer:
         return t.view(self.torch.bfloat16) if self.cfg.act == W.BF16 else t
 
     def run(self, x) -> dict:
-        torch = self.torch
         T = x.shape[0]
+        self.layer.forward(self.x_tensor(x), T)
+        return self.collect(T)
+
+    def run_ids(self, x, ids, w) -> dict:
+        """moe_permute -> moe_grouped_ffn -> moe_combine on caller-given routing
+        (ids [T, k] in [0, E), weights w [T, k]); no router call."""
+        torch = self.torch
+        T, k = ids.shape
         L = self.layer
-        y = L.forward(self.x_tensor(x), T)
+        L.ids[:T * k].copy_(torch.from_numpy(np.ascontiguousarray(ids, np.int32).reshape(-1)))
+        L.w[:T * k].copy_(torch.from_numpy(np.ascontiguousarray(w, np.float32).reshape(-1)))
+        xt = self.x_tensor(x)
+        L.permute(T)
+        L.grouped_ffn(xt, T)
+        L.combine(T)
+        out = self.collect(T)
+        out.pop("logits")
+        return out
+
+    def collect(self, T) -> dict:
+        torch = self.torch
         torch.cuda.synchronize()
+        L = self.layer
+        y = L.y[:T]
         n = T * self.cfg.k
         cpu = lambda t: t.cpu().numpy()
         out = dict(logits=cpu(L.logits[:T]), ids=cpu(L.ids[:n]).reshape(T, self.cfg.k),
@@ -86,9 +106,39 @@ def assert_close(a, ref, fp32: bool, what: str):
     return r
 
 
+def _stored_f64(a, fmt):
+    """Exact fp64 values of stored activations / router weights (bf16 bits or fp32)."""
+    if fmt == W.BF16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, np.float64)
+
+
+def logit_error_bound(cfg, inputs, tokens):
+    """Per-element bound on |fp32 logit - exact logit| [n, E].
+
+    bf16 router: every product x_i w_i is exact in fp32, so the error is that of
+    the fp32 sums.  The kernels sum K in 8 slices of d/8, each an MFMA chain
+    of d/256 steps of 32 elements, then the 8 slices, then the bias.  A term
+    passes at most log2(32) + 1 = 6 roundings inside one MFMA step and one per
+    later step and slice addition, so with m = 6 d/256 + 8 + 1 roundings the
+    error is at most m u sum_i |x_i w_i| (u = 2^-24; first order, m u << 1).
+    The MFMA's internal rounding is not documented, so each rounding is
+    allowed 2u (a truncating adder's worst case).  fp32 router: one fused
+    multiply-add per element in sequence, m = d + 1."""
+    x = _stored_f64(inputs["x"], cfg.act)[np.asarray(tokens)]
+    wr = _stored_f64(inputs["wr"], cfg.act)
+    m = cfg.d + 1 if cfg.act == W.F32 else 6 * (cfg.d // 256) + 9
+    gamma = 2 * m * 2.0 ** -24
+    absdot = np.abs(x) @ np.abs(wr).T
+    if inputs.get("bias") is not None:
+        absdot += np.abs(inputs["bias"].astype(np.float64))[None, :]
+    return gamma * absdot * 1.01 + 1e-30
+
+
 def check_route(cfg, inputs, out, tokens=None):
     """ids bit-exact and w close against the oracle fed the GPU's fp32 logits;
-    GPU logits close to the oracle's own fp64 logits."""
+    every GPU logit within the fp32 summation bound of the oracle's exact
+    (fp64) logit."""
     T = out["ids"].shape[0]
     L64 = out["logits"].astype(np.float64)
     ids_o, w_o = oracle.topk_softmax(L64, cfg.k)
@@ -97,8 +147,11 @@ def check_route(cfg, inputs, out, tokens=None):
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     lo = oracle.router_logits(inputs["x"], ORC_FMT[cfg.act], inputs["wr"], ORC_FMT[cfg.act],
                               cfg.d, cfg.E, bias=inputs.get("bias"), tokens=tok)
-    err = np.max(np.abs(out["logits"][tok].astype(np.float64) - lo))
-    assert err <= 2e-4 * max(1.0, np.max(np.abs(lo))), f"router logits max err {err:.3e}"
+    err = np.abs(out["logits"][tok].astype(np.float64) - lo)
+    bound = logit_error_bound(cfg, inputs, tok)
+    bad = err > bound
+    assert not bad.any(), (f"router logits: {int(bad.sum())} beyond the fp32 bound, worst "
+                           f"err {err[bad].max():.3e} vs {bound[bad][np.argmax(err[bad])]:.3e}")
     return ids_o, w_o
 
 
