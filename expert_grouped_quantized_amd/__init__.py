@@ -11,7 +11,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB_OVERRIDE names another build of the same ABI (the host tests point it
+# at a sanitizer build of the host side); by default the in-tree libmoe.so.
+LIB_PATH = os.environ.get("MOE_LIB_OVERRIDE") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EDEVICE = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_I4_G32, MOE_I8_ROW = 0, 1, 2, 3
