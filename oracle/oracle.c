@@ -9,10 +9,11 @@
  * What it follows (the web pages on serving Qwen3.8-Flash-Next):
  *   - "Qwen3.8-Flash-Next" (TandemLLM docs, chapter 17), Table 17.1: each
  *     token runs 10 routed experts out of 512 plus 1 shared expert.
- *   - "Qwen3.8-Flash-Next-Dual-GPU" README, section "Dedicated prefill lane":
- *     a deterministic expert-major route plan, per-expert matrix work, router
- *     weights folded into the intermediate activation, one output per
- *     assignment, and a fixed-order reduction of each token's routes.
+ *   - "Qwen3.8-Flash-Next-Dual-GPU" README, section "Dedicated prefill lane"
+ *     (its numbered list): assignments grouped by expert in a reproducible
+ *     order, each expert's matrices applied to its group, the routing weight
+ *     applied to the intermediate before the down projection, a separate
+ *     result per assignment, and each token's results added in slot order.
  *   - same README, section "Independent decode lane": the 512-expert router
  *     uses a deterministic stable top-k.
  *   - same README, "Model artifact and memory placement" table: symmetric
