@@ -56,6 +56,14 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "expert_grouped_quantized_amd.build.build()")
+        # torch carries its own HIP runtime (soname libamdhip64.so.7).  Load it
+        # first, so that libmoe.so binds to that same runtime instead of
+        # loading a second one from the ROCm install, which would not share
+        # torch's device memory and streams.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
         D = ctypes.POINTER(Desc)
@@ -71,6 +79,7 @@ def lib():
             "moe_route_from_logits": ([D, i32, i32, vp, vp, vp, vp], i32),
             "moe_permute": ([D, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
             "moe_grouped_ffn": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+            "moe_grouped_ffn_noalloc": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "moe_combine": ([D, i32, i32, vp, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -173,6 +182,14 @@ def moe_grouped_ffn(desc, T, k, hidden, topk_w, offsets, perm, routed_blob, shar
                                  _p(perm), _p(routed_blob), _p(shared_blob), _p(out_assign),
                                  _p(shared_out), _p(workspace), wsb, _stream(stream)),
            "moe_grouped_ffn")
+
+
+def moe_grouped_ffn_noalloc(desc, T, k, hidden, topk_w, offsets, perm, routed_blob, shared_blob,
+                            out_assign, shared_out, stream=None):
+    _check(lib().moe_grouped_ffn_noalloc(ctypes.byref(desc), T, k, _p(hidden), _p(topk_w),
+                                         _p(offsets), _p(perm), _p(routed_blob),
+                                         _p(shared_blob), _p(out_assign), _p(shared_out),
+                                         _stream(stream)), "moe_grouped_ffn_noalloc")
 
 
 def moe_combine(desc, T, k, out_assign, inv_perm, shared_out, y, stream=None):

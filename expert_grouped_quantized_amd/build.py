@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["route.hip", "permute.hip", "ffn.hip", "ffn_lowbit.hip", "ffn_mx.hip", "combine.hip",
-           "abi.cpp"]
+           "noalloc.hip", "abi.cpp"]
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # keep the compiler from emitting packed-fp32 VALU instructions
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

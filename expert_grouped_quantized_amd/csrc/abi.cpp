@@ -488,6 +488,66 @@ moe_status pack_or_unpack(const moe_desc* D, int32_t kind, const void* gate, con
 
 }  // namespace
 
+moe_status moe::grouped_ffn_call(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
+                                 const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                                 const void* routed_blob, const void* shared_blob,
+                                 float* out_assign, float* shared_out, void* workspace,
+                                 size_t ws_bytes, ScratchFn scratch, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(hidden, "hidden"));
+  TRY(check_ptr(topk_w, "topk_w"));
+  TRY(check_ptr(offsets, "offsets"));
+  TRY(check_ptr(perm, "perm"));
+  TRY(check_ptr(routed_blob, "routed_blob"));
+  TRY(check_ptr(out_assign, "out_assign"));
+  if (!scratch) TRY(check_ptr(workspace, "workspace", 256));
+  if (D->n_shared) {
+    TRY(check_ptr(shared_blob, "shared_blob"));
+    TRY(check_ptr(shared_out, "shared_out"));
+  } else if (shared_blob || shared_out) {
+    return fail(MOE_EINVAL, "shared_blob/shared_out must be NULL when n_shared == 0");
+  }
+  const WsLayout L = ws_layout(*D, T, k);
+  if (ws_bytes < L.total) {
+    if (scratch)
+      return fail(MOE_EWORKSPACE,
+                  "T=%d, k=%d need %zu bytes of scratch; the library's static scratch holds "
+                  "%zu (use moe_grouped_ffn with a workspace)",
+                  T, k, L.total, ws_bytes);
+    return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  }
+  if (T == 0) return ok();
+  if (scratch) {
+    const hipError_t e = scratch(&workspace);
+    if (e != hipSuccess) return device_result(e, "scratch address");
+  }
+  uint8_t* w = (uint8_t*)workspace;
+  FfnArgs a{};
+  a.T = T; a.k = k; a.d = D->d; a.E = D->n_experts; a.F = D->ffn;
+  a.Fs = D->n_shared ? D->shared_ffn : 0; a.n_shared = D->n_shared;
+  a.routed_fmt = D->expert_w; a.shared_fmt = D->shared_w;
+  a.routed_slots = L.routed_slots;
+  a.shared_slots = D->n_shared ? (T + BM - 1) / BM : 0;
+  a.hidden = hidden; a.topk_w = topk_w; a.offsets = offsets; a.perm = perm;
+  a.tiles = (const int4*)(w + L.tiles);
+  a.routed_blob = (const uint8_t*)routed_blob;
+  a.shared_blob = (const uint8_t*)shared_blob;
+  a.h_routed = w + L.h_routed; a.h_shared = w + L.h_shared;
+  a.x16 = (uint16_t*)(w + L.x16); a.xscale = (float*)(w + L.xexp);
+  a.xq = w + L.x16; a.xsc = w + L.xexp;
+  a.hq = w + L.h_routed; a.hsc = w + L.h_scale;
+  a.out_assign = out_assign; a.shared_out = shared_out;
+  hipStream_t s = (hipStream_t)stream;
+  if (scratch) {
+    const hipError_t e = launch_tiles_from_offsets(D->n_experts, tile_rows(T), L.routed_slots,
+                                                   offsets, (int4*)(w + L.tiles), s);
+    if (e != hipSuccess) return device_result(e, "row-tile plan launch");
+  }
+  return device_result(D->act == MOE_F32 ? launch_ffn_f32(a, s) : launch_ffn_bf16(a, s),
+                       "grouped-ffn launch");
+}
+
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -595,44 +655,8 @@ moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* 
                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
                            const void* routed_blob, const void* shared_blob, float* out_assign,
                            float* shared_out, void* workspace, size_t ws_bytes, void* stream) {
-  TRY(check_desc(D));
-  TRY(check_tk(D, T, k));
-  TRY(check_ptr(hidden, "hidden"));
-  TRY(check_ptr(topk_w, "topk_w"));
-  TRY(check_ptr(offsets, "offsets"));
-  TRY(check_ptr(perm, "perm"));
-  TRY(check_ptr(routed_blob, "routed_blob"));
-  TRY(check_ptr(out_assign, "out_assign"));
-  TRY(check_ptr(workspace, "workspace", 256));
-  if (D->n_shared) {
-    TRY(check_ptr(shared_blob, "shared_blob"));
-    TRY(check_ptr(shared_out, "shared_out"));
-  } else if (shared_blob || shared_out) {
-    return fail(MOE_EINVAL, "shared_blob/shared_out must be NULL when n_shared == 0");
-  }
-  const WsLayout L = ws_layout(*D, T, k);
-  if (ws_bytes < L.total)
-    return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
-  if (T == 0) return ok();
-  uint8_t* w = (uint8_t*)workspace;
-  FfnArgs a{};
-  a.T = T; a.k = k; a.d = D->d; a.E = D->n_experts; a.F = D->ffn;
-  a.Fs = D->n_shared ? D->shared_ffn : 0; a.n_shared = D->n_shared;
-  a.routed_fmt = D->expert_w; a.shared_fmt = D->shared_w;
-  a.routed_slots = L.routed_slots;
-  a.shared_slots = D->n_shared ? (T + BM - 1) / BM : 0;
-  a.hidden = hidden; a.topk_w = topk_w; a.offsets = offsets; a.perm = perm;
-  a.tiles = (const int4*)(w + L.tiles);
-  a.routed_blob = (const uint8_t*)routed_blob;
-  a.shared_blob = (const uint8_t*)shared_blob;
-  a.h_routed = w + L.h_routed; a.h_shared = w + L.h_shared;
-  a.x16 = (uint16_t*)(w + L.x16); a.xscale = (float*)(w + L.xexp);
-  a.xq = w + L.x16; a.xsc = w + L.xexp;
-  a.hq = w + L.h_routed; a.hsc = w + L.h_scale;
-  a.out_assign = out_assign; a.shared_out = shared_out;
-  hipStream_t s = (hipStream_t)stream;
-  return device_result(D->act == MOE_F32 ? launch_ffn_f32(a, s) : launch_ffn_bf16(a, s),
-                       "grouped-ffn launch");
+  return grouped_ffn_call(D, T, k, hidden, topk_w, offsets, perm, routed_blob, shared_blob,
+                          out_assign, shared_out, workspace, ws_bytes, nullptr, stream);
 }
 
 moe_status moe_combine(const moe_desc* D, int32_t T, int32_t k, const float* out_assign,

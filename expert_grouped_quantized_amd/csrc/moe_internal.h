@@ -186,5 +186,21 @@ hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,
                           const int32_t* inv_perm, const float* shared_out, void* y,
                           hipStream_t s);
+// the route plan's row tiles rebuilt from its offsets alone
+hipError_t launch_tiles_from_offsets(int E, int rows, int slots, const int32_t* offsets,
+                                     int4* tiles, hipStream_t s);
+
+// moe_grouped_ffn's checks and launches.  With scratch == nullptr the
+// intermediates go to the caller's workspace `ws` of ws_bytes, where
+// moe_permute left the row-tile plan.  Otherwise `ws` is ignored: once every
+// argument has passed its checks and T > 0, scratch() gives the address of a
+// library-held region of ws_bytes (moe_grouped_ffn_noalloc), and the row-tile
+// plan is first rebuilt there from `offsets`.
+typedef hipError_t (*ScratchFn)(void** address);
+moe_status grouped_ffn_call(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
+                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                            const void* routed_blob, const void* shared_blob, float* out_assign,
+                            float* shared_out, void* ws, size_t ws_bytes, ScratchFn scratch,
+                            void* stream);
 
 }  // namespace moe

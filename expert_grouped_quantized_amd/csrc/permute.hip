@@ -62,6 +62,38 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return r;
 }
 
+// Row tiles of the grouped GEMMs (thread e < E holds expert e's row count
+// `total` and first row `off`): expert e owns ceil(total / rows) tiles, each
+// stored resolved as (expert, first row, rows) so a GEMM block finds its rows
+// with one load; the slots past the plan's tiles, up to `slots`, get 0 rows.
+// Every thread of the block must call it.
+__device__ void write_row_tiles(int E, int rows, int slots, int total, int off, int* wsum,
+                                int* total_all, int4* __restrict__ tiles) {
+  const int tid = threadIdx.x;
+  const int nt = tid < E ? (total + rows - 1) / rows : 0;
+  const int tstart = block_exclusive_scan(nt, wsum, total_all);
+  for (int j = 0; j < nt; j++)
+    tiles[tstart + j] = make_int4(tid, off + j * rows, min(rows, total - j * rows), 0);
+  for (int j = *total_all + tid; j < slots; j += PLAN_THREADS) tiles[j] = make_int4(0, 0, 0, 0);
+}
+
+// The row tiles alone, from a finished plan's offsets (one block).
+__global__ __launch_bounds__(PLAN_THREADS) void tiles_from_offsets_kernel(
+    int E, int rows, int slots, const int32_t* __restrict__ offsets, int4* __restrict__ tiles) {
+  __shared__ int wsum[PLAN_WAVES];
+  __shared__ int total_all;
+  const int tid = threadIdx.x;
+  const int off = tid < E ? offsets[tid] : 0;
+  const int total = tid < E ? offsets[tid + 1] - off : 0;
+  write_row_tiles(E, rows, slots, total, off, wsum, &total_all, tiles);
+}
+
+hipError_t launch_tiles_from_offsets(int E, int rows, int slots, const int32_t* offsets,
+                                     int4* tiles, hipStream_t s) {
+  tiles_from_offsets_kernel<<<1, PLAN_THREADS, 0, s>>>(E, rows, slots, offsets, tiles);
+  return hipGetLastError();
+}
+
 template <bool SINGLE>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     int n, int E, int n_chunks, const int32_t* __restrict__ ids,
@@ -123,15 +155,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
   if (chunk == 0) {
     if (tid < E) offsets[tid] = off;
     if (tid == 0) offsets[E] = n;
-    // 3) row tiles of the grouped GEMMs: expert e owns ceil(total/rows)
-    //    tiles, each stored resolved (expert, first row, rows) so a GEMM block
-    //    finds its rows with one load; the slots past the plan's tiles hold 0
-    //    rows
-    const int nt = tid < E ? (total + rows - 1) / rows : 0;
-    const int tstart = block_exclusive_scan(nt, wsum, &total_all);
-    for (int j = 0; j < nt; j++)
-      tiles[tstart + j] = make_int4(tid, off + j * rows, min(rows, total - j * rows), 0);
-    for (int j = total_all + tid; j < slots; j += PLAN_THREADS) tiles[j] = make_int4(0, 0, 0, 0);
+    // 3) row tiles of the grouped GEMMs
+    write_row_tiles(E, rows, slots, total, off, wsum, &total_all, tiles);
   }
   __syncthreads();
 

@@ -247,6 +247,24 @@ moe_status moe_grouped_ffn(const moe_desc* desc, int32_t T, int32_t k, const voi
                            float* shared_out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* moe_grouped_ffn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs and arithmetic as moe_grouped_ffn, minus the
+ * workspace: the row-tile plan is rebuilt from `offsets` (so moe_permute's
+ * plan in a workspace is not needed) and every intermediate lives in a
+ * scratch array of 8 MiB that the library keeps on each GPU it runs on until
+ * the process ends.  A call whose moe_workspace_bytes(desc, T, k) exceeds
+ * 8 MiB returns MOE_EWORKSPACE and enqueues nothing (d=2560, ffn=1024,
+ * k=10, int4 routed and int8 shared experts: up to T = 302).  The first
+ * call on a GPU looks up that GPU's scratch address (hipGetSymbolAddress; no
+ * allocation).  Calls that overlap on one GPU -- from two streams or two
+ * threads -- share the scratch and race: the caller must order them.       */
+moe_status moe_grouped_ffn_noalloc(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
+                                   const float* topk_w, const int32_t* offsets,
+                                   const int32_t* perm, const void* routed_blob,
+                                   const void* shared_blob, float* out_assign, float* shared_out,
+                                   void* stream);
+
 /* Fixed-order combine ("Dedicated prefill lane", step 5), no atomics:
  *   y[t] = act( ((out_assign[inv_perm[t*k+0]] + ... ) + out_assign[inv_perm[t*k+k-1]])
  *               + shared_out[t] )

@@ -32,4 +32,21 @@ hipError_t launch_combine(int, int, int, int, const float*, const int32_t*, cons
                           hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_tiles_from_offsets(int, int, int, const int32_t*, int4*, hipStream_t) {
+  return hipErrorNoDevice;
+}
 }  // namespace moe
+
+// The no-allocation entry point of noalloc.hip (a device-side source): the
+// same host checks, with a scratch lookup that reports no device.
+static hipError_t no_scratch(void**) { return hipErrorNoDevice; }
+extern "C" moe_status moe_grouped_ffn_noalloc(const moe_desc* desc, int32_t T, int32_t k,
+                                              const void* hidden, const float* topk_w,
+                                              const int32_t* offsets, const int32_t* perm,
+                                              const void* routed_blob, const void* shared_blob,
+                                              float* out_assign, float* shared_out,
+                                              void* stream) {
+  return moe::grouped_ffn_call(desc, T, k, hidden, topk_w, offsets, perm, routed_blob,
+                               shared_blob, out_assign, shared_out, nullptr, size_t(8) << 20,
+                               no_scratch, stream);
+}
