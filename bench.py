@@ -82,7 +82,7 @@ class Setup:
         L.route(self.x, self.T)
         if ev is not None:
             ev[1].record()
-        L.permute(self.T)
+        L.permute(self.x, self.T)
         if ev is not None:
             ev[2].record()
         L.grouped_ffn(self.x, self.T)

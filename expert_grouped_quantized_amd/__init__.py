@@ -77,7 +77,7 @@ def lib():
             "moe_workspace_bytes": ([D, i32, i32, ctypes.POINTER(sz)], i32),
             "moe_route": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
             "moe_route_from_logits": ([D, i32, i32, vp, vp, vp, vp], i32),
-            "moe_permute": ([D, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
+            "moe_permute": ([D, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
             "moe_grouped_ffn": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
             "moe_grouped_ffn_noalloc": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "moe_combine": ([D, i32, i32, vp, vp, vp, vp, vp], i32),
@@ -168,16 +168,23 @@ def moe_route_from_logits(desc, T, k, logits, topk_ids, topk_w, stream=None):
                                        _p(topk_w), _stream(stream)), "moe_route_from_logits")
 
 
-def moe_permute(desc, T, k, topk_ids, offsets, perm, inv_perm, workspace, workspace_bytes=None,
-                stream=None):
-    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    _check(lib().moe_permute(ctypes.byref(desc), T, k, _p(topk_ids), _p(offsets), _p(perm),
-                             _p(inv_perm), _p(workspace), wsb, _stream(stream)), "moe_permute")
+def _ws_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return workspace_bytes
+    return workspace.numel() * workspace.element_size()
+
+
+def moe_permute(desc, T, k, hidden, topk_ids, offsets, perm, inv_perm, workspace,
+                workspace_bytes=None, stream=None):
+    _check(lib().moe_permute(ctypes.byref(desc), T, k, _p(hidden), _p(topk_ids), _p(offsets),
+                             _p(perm), _p(inv_perm), _p(workspace),
+                             _ws_bytes(workspace, workspace_bytes), _stream(stream)),
+           "moe_permute")
 
 
 def moe_grouped_ffn(desc, T, k, hidden, topk_w, offsets, perm, routed_blob, shared_blob,
                     out_assign, shared_out, workspace, workspace_bytes=None, stream=None):
-    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    wsb = _ws_bytes(workspace, workspace_bytes)
     _check(lib().moe_grouped_ffn(ctypes.byref(desc), T, k, _p(hidden), _p(topk_w), _p(offsets),
                                  _p(perm), _p(routed_blob), _p(shared_blob), _p(out_assign),
                                  _p(shared_out), _p(workspace), wsb, _stream(stream)),

@@ -5,62 +5,16 @@
 
 namespace moe {
 
-// Activations of an int4 layer as fp16: each token row is scaled by 2^-e so
-// its largest magnitude lies in [2^14, 2^15) -- every bf16 value of the row is
-// then exact in fp16 unless it is 2^-28 below the row's largest -- and 2^e is
-// kept for the gate/up epilogue.  One wave per row; each lane reads its
-// pieces XB at a time with no condition on the loads (indices past the row
-// re-read its last piece: harmless for the maximum, and never stored), so a
-// batch is in flight at once instead of one load per round trip.
-constexpr int XB = 8;  // 16-byte pieces per lane per batch (d <= 4096 in one)
+// Activations of an int4 layer as fp16 (calls of more than 32 tokens): each
+// token row scaled by 2^-e (row_fp16_exponent), 2^e kept for the gate/up
+// epilogue; one wave per row.  (For calls of at most 32 tokens moe_permute's
+// plan launch writes the same copy from blocks of its own.)
 __global__ __launch_bounds__(256) void x_to_f16_kernel(int T, int d, const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ x16,
                                                        float* __restrict__ xscale) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const u32x4_t* src = (const u32x4_t*)(x + (size_t)t * d);
-  const int pieces = d / 8;
-  uint32_t mx = 0;  // largest |x| as float bits (non-negative floats order as integers)
-  for (int p0 = 0; p0 < pieces; p0 += 64 * XB) {
-    u32x4_t v[XB];
-#pragma unroll
-    for (int j = 0; j < XB; j++) v[j] = src[min(p0 + 64 * j + lane, pieces - 1)];
-#pragma unroll
-    for (int j = 0; j < XB; j++)
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const uint32_t a = (v[j][w] << 16) & 0x7fffffffu, b = v[j][w] & 0x7fff0000u;
-        mx = max(mx, max(a, b));
-      }
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-  int e = 0;
-  if (mx != 0) {
-    const int ex = (int)(mx >> 23) - 127;  // floor(log2 max|x|) for normal values
-    e = max(ex, -126) - 14;
-    e = max(e, -100);
-  }
-  const float down = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
-  if (lane == 0) xscale[t] = __uint_as_float((uint32_t)(127 + e) << 23);
-  u32x4_t* dst = (u32x4_t*)(x16 + (size_t)t * d);
-  for (int p0 = 0; p0 < pieces; p0 += 64 * XB) {
-    u32x4_t v[XB];
-#pragma unroll
-    for (int j = 0; j < XB; j++) v[j] = src[min(p0 + 64 * j + lane, pieces - 1)];
-#pragma unroll
-    for (int j = 0; j < XB; j++) {
-      const int p = p0 + 64 * j + lane;
-      u32x4_t o;
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        f16x2_t h = {(_Float16)(bf16_lo(v[j][w]) * down), (_Float16)(bf16_hi(v[j][w]) * down)};
-        o[w] = __builtin_bit_cast(uint32_t, h);
-      }
-      if (p < pieces) dst[p] = o;
-    }
-  }
+  wave_row_to_f16(t, d, x, x16, xscale);
 }
 
 hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s) {

@@ -349,7 +349,9 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
   const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
   const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
-  if (x16_path(RF, MAXMF)) {
+  // calls of at most 32 tokens get their fp16 copy of x from moe_permute's
+  // plan launch (one launch fewer on the decode path)
+  if (x16_path(RF, MAXMF) && MAXMF > 2) {
     hipError_t e = launch_x_to_f16(a, s);
     if (e != hipSuccess) return e;
   }

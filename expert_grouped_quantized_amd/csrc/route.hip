@@ -7,8 +7,7 @@
 // order-preserving logit keys, equal keys resolved to the lower expert id --
 // the deterministic stable top-k of the README's "Independent decode lane".
 // Routing weights: softmax over the k chosen logits.
-#include "device_common.h"
-#include "moe_internal.h"
+#include "route_kernels.h"
 
 namespace moe {
 
@@ -22,68 +21,13 @@ namespace moe {
 //    router rows are both staged through LDS with four chunks of loads in
 //    flight.
 
-typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_r, a),
-                                                 __builtin_bit_cast(bf16x8_r, b), c, 0, 0, 0);
-}
-
-constexpr int RS_WAVES = 8, RS_EXPERTS = 16;
-
 template <int MF>
 __global__ __launch_bounds__(RS_WAVES * 64) void router_small_kernel(
     int T, int d, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits) {
   __shared__ f32x4_t part[RS_WAVES][MF][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = blockIdx.x * RS_EXPERTS;
-  const int kw = d / RS_WAVES;  // multiple of 32 (d % 256 == 0)
-  const int kb = wave * kw + 8 * (lane >> 4);
-  const int er = e0 + (lane & 15);
-  const uint16_t* bp = er < E ? wr + (size_t)er * d + kb : nullptr;
-  const uint16_t* ap[MF];
-#pragma unroll
-  for (int m = 0; m < MF; m++) {
-    const int t = m * 16 + (lane & 15);
-    ap[m] = t < T ? x + (size_t)t * d + kb : nullptr;
-  }
-  f32x4_t acc[MF];
-#pragma unroll
-  for (int m = 0; m < MF; m++) acc[m] = f32x4_t{0, 0, 0, 0};
-  const u32x4_t zero = {0, 0, 0, 0};
-  constexpr int U = 10;  // K steps whose loads are all issued before their MFMAs
-  for (int k0 = 0; k0 < kw; k0 += 32 * U) {
-    u32x4_t bv[U], av[U][MF];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int k = k0 + 32 * u;
-      const bool in = k < kw;
-      bv[u] = (in && bp) ? *(const u32x4_t*)(bp + k) : zero;
-#pragma unroll
-      for (int m = 0; m < MF; m++) av[u][m] = (in && ap[m]) ? *(const u32x4_t*)(ap[m] + k) : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++)
-#pragma unroll
-      for (int m = 0; m < MF; m++) acc[m] = mfma16(av[u][m], bv[u], acc[m]);
-  }
-#pragma unroll
-  for (int m = 0; m < MF; m++) part[wave][m][lane] = acc[m];
-  __syncthreads();
-  if (wave < MF) {  // wave m finishes token fragment m
-    f32x4_t s = part[0][wave][lane];
-#pragma unroll
-    for (int w = 1; w < RS_WAVES; w++) s += part[w][wave][lane];
-    const int e = e0 + (lane & 15);
-    if (e < E) {
-      const float bv = bias ? bias[e] : 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int t = wave * 16 + 4 * (lane >> 4) + r;
-        if (t < T) logits[(size_t)t * E + e] = s[r] + bv;
-      }
-    }
-  }
+  router_small_block<MF>(T, d, E, x, wr, bias, logits, blockIdx.x * RS_EXPERTS, 0,
+                         threadIdx.x >> 6, part, [] { __syncthreads(); });
 }
 
 constexpr int RL_M = 64, RL_N = 128, RL_LEAD = 4;
@@ -243,101 +187,15 @@ hipError_t launch_router_f32(int T, int d, int E, const float* x, const float* w
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- top-k
-// Order-preserving map of a finite float to uint32 (larger float -> larger
-// key); -0.0 is first made +0.0 so the two tie.  No finite float maps to 0,
-// which marks an absent or already chosen candidate.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-// Cross-lane steps inside a 16-lane row (DPP), then the four row results
-// combined through scalar reads: every lane gets the same answer, and the
-// combining order is fixed.
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // lane ^ 2
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
-  const uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
-  return op(op(a, b), op(c, d));
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  auto add = [](uint32_t x, uint32_t y) { return __float_as_uint(__uint_as_float(x) + __uint_as_float(y)); };
-  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), add));
-}
-
-// One wave per token; 4 tokens per 256-thread block.  Expert e lives in lane
-// e % 64, slot e / 64 (coalesced loads); PL slots a lane (8 for E <= 512, 16
-// for E <= 1024).  Each lane keeps its best remaining candidate (largest key,
-// lowest slot among equal keys).  Each of the k rounds takes a wave max of
-// those keys and -- only when several lanes hold that key -- a wave min of
-// their expert ids, so equal logits go to the lower id; only the winning lane
-// then rescans its slots.
+// One wave per token, 4 tokens per 256-thread block (topk_wave).
 template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k,
                                                    const float* __restrict__ logits,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  // The PL loads carry no condition (slots past E re-read the row's last
-  // logit), so they issue back to back under one wait; a per-slot guarded
-  // load would wait for each in turn.
-  uint32_t key[PL];
-  float lv[PL];
-  const float* row = logits + (size_t)t * E;
-#pragma unroll
-  for (int j = 0; j < PL; j++) lv[j] = row[min(j * 64 + lane, E - 1)];
-#pragma unroll
-  for (int j = 0; j < PL; j++) key[j] = j * 64 + lane < E ? order_key(lv[j]) : 0u;
-  auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
-  auto umin = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
-  uint32_t bk = 0;
-  int bj = 0;
-  auto lane_best = [&]() {
-    bk = 0;
-    bj = 0;
-#pragma unroll
-    for (int j = 0; j < PL; j++)
-      if (key[j] > bk) { bk = key[j]; bj = j; }
-  };
-  lane_best();
-  int my_id = 0;
-  float my_logit = 0.0f, top_logit = 0.0f;
-  for (int s = 0; s < k; s++) {
-    const uint32_t m = wave_reduce_u32(bk, umax);
-    const uint64_t holders = __ballot(bk == m);
-    const uint32_t my_e = (uint32_t)(bj * 64 + lane);
-    uint32_t e;
-    if (__popcll(holders) == 1)
-      e = (uint32_t)__builtin_amdgcn_readlane((int)my_e, __ffsll((long long)holders) - 1);
-    else
-      e = wave_reduce_u32(bk == m ? my_e : 0xFFFFFFFFu, umin);
-    if (my_e == e) {  // the winning lane drops the candidate and rescans
-#pragma unroll
-      for (int j = 0; j < PL; j++)
-        if (j == bj) key[j] = 0u;
-      lane_best();
-    }
-    const float lg = key_to_float(m);
-    if (s == 0) top_logit = lg;
-    if (s == lane) { my_id = (int)e; my_logit = lg; }
-  }
-  const float ex = lane < k ? expf(my_logit - top_logit) : 0.0f;
-  const float sum = wave_sum_f32(ex);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = ex / sum;
-  }
+  topk_wave<PL>(t, E, k, logits, ids, w);
 }
 
 hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w,

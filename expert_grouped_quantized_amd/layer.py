@@ -49,8 +49,8 @@ class MoELayer:
         moe_route(self.desc, T, self.k, x, self.router_w, self.bias, self.logits, self.ids,
                   self.w)
 
-    def permute(self, T):
-        moe_permute(self.desc, T, self.k, self.ids, self.offsets, self.perm, self.inv_perm,
+    def permute(self, x, T):
+        moe_permute(self.desc, T, self.k, x, self.ids, self.offsets, self.perm, self.inv_perm,
                     self.workspace, self.ws_bytes)
 
     def grouped_ffn(self, x, T):
@@ -66,7 +66,7 @@ class MoELayer:
         T = x.shape[0] if T is None else T
         assert T <= self.T_max
         self.route(x, T)
-        self.permute(T)
+        self.permute(x, T)
         self.grouped_ffn(x, T)
         self.combine(T)
         return self.y[:T]

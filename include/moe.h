@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -168,7 +168,7 @@ moe_status moe_unpack_experts(const moe_desc* desc, int32_t kind, const void* bl
                               void* up_scales, void* down, void* down_scales);
 
 /* Bytes of device workspace that moe_permute and moe_grouped_ffn need for T
- * tokens and top-k.  Host only.                                             */
+ * tokens and top-k.  Nothing in it needs initializing.  Host only.         */
 moe_status moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t k, size_t* bytes);
 
 /* ------------------------------------------------------------------ device */
@@ -194,18 +194,25 @@ moe_status moe_route_from_logits(const moe_desc* desc, int32_t T, int32_t k, con
 
 /* Route plan ("Dedicated prefill lane", step 1): the assignments ordered by
  * expert, the same order on every run.
+ *   hidden    [T, d] act dtype, the layer's input (read only by int4 and b-bit
+ *             layers at T <= 32: see workspace)
  *   topk_ids  [T*k] int32, flat index f = t*k + s, values in [0, E)
  *   offsets   [E+1] int32 out: offsets[e] = #{f : ids[f] < e}; offsets[E] = T*k
  *   perm      [T*k] int32 out: the f of expert e, ascending, at
  *             perm[offsets[e] .. offsets[e+1])
  *   inv_perm  [T*k] int32 out: inv_perm[perm[p]] = p
  *   workspace scratch of >= moe_workspace_bytes(desc, T, k); this call also
- *             leaves in it the row-tile plan that moe_grouped_ffn reads, so
- *             pass the same workspace, unchanged, to the moe_grouped_ffn call
- *             that consumes this plan.                                      */
-moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const int32_t* topk_ids,
-                       int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* workspace,
-                       size_t workspace_bytes, void* stream);
+ *             leaves in it what moe_grouped_ffn reads besides its arguments --
+ *             the row-tile plan, and for int4 / b-bit layers at T <= 32 the
+ *             fp16 copy of hidden that their gate/up products run on (each
+ *             token row scaled by a power of two; moe_grouped_ffn makes it
+ *             itself at larger T) -- so pass the same workspace, unchanged,
+ *             and the same hidden to the moe_grouped_ffn call that consumes
+ *             this plan.                                                   */
+moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
+                       const int32_t* topk_ids, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_perm, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* Expert-grouped SwiGLU ("Dedicated prefill lane", steps 2-4).  For each
  * expert e and each p in [offsets[e], offsets[e+1]), with f = perm[p],

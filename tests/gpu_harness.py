@@ -58,7 +58,7 @@ class GpuLayer:
         L.ids[:T * k].copy_(torch.from_numpy(np.ascontiguousarray(ids, np.int32).reshape(-1)))
         L.w[:T * k].copy_(torch.from_numpy(np.ascontiguousarray(w, np.float32).reshape(-1)))
         xt = self.x_tensor(x)
-        L.permute(T)
+        L.permute(xt, T)
         L.grouped_ffn(xt, T)
         L.combine(T)
         out = self.collect(T)

@@ -19,8 +19,8 @@ hipError_t launch_router_f32(int, int, int, const float*, const float*, const fl
 hipError_t launch_topk(int, int, int, const float*, int32_t*, float*, hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t launch_plan(int, int, int, const int32_t*, int32_t*, int32_t*, int32_t*, void*,
-                       const WsLayout&, hipStream_t) {
+hipError_t launch_plan(int, int, int, int, const int32_t*, int32_t*, int32_t*, int32_t*, void*,
+                       const WsLayout&, int, const uint16_t*, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_ffn_bf16(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
@@ -32,7 +32,8 @@ hipError_t launch_combine(int, int, int, int, const float*, const int32_t*, cons
                           hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t launch_tiles_from_offsets(int, int, int, const int32_t*, int4*, hipStream_t) {
+hipError_t launch_tiles_from_offsets(int, int, int, const int32_t*, int4*, int, int,
+                                     const uint16_t*, uint16_t*, float*, hipStream_t) {
   return hipErrorNoDevice;
 }
 }  // namespace moe

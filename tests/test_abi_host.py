@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert M.moe_abi_version() == 1
+    assert M.moe_abi_version() == 2
     assert M.moe_status_str(0) == "ok"
     assert M.moe_status_str(-3) == "workspace too small"
     assert M.moe_status_str(12345) == "unknown status"
@@ -95,20 +95,25 @@ def test_T_zero_is_ok_and_launches_nothing():
     desc = _desc()
     ws = M.moe_workspace_bytes(desc, 0, 10)
     L = M.lib()
-    assert L.moe_permute(ctypes.byref(desc), 0, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 0
+    assert L.moe_permute(ctypes.byref(desc), 0, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                         None) == 0
     assert L.moe_combine(ctypes.byref(desc), 0, 10, FAKE, FAKE, FAKE, FAKE, None) == 0
 
 
 def test_workspace_too_small():
     desc = _desc()
     need = M.moe_workspace_bytes(desc, 64, 10)
-    rc = M.lib().moe_permute(ctypes.byref(desc), 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
-                             None)
+    rc = M.lib().moe_permute(ctypes.byref(desc), 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             need - 1, None)
     assert rc == M.MOE_EWORKSPACE
     assert "workspace" in M.moe_last_error()
-    rc = M.lib().moe_permute(ctypes.byref(desc), 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
+    rc = M.lib().moe_permute(ctypes.byref(desc), 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
                              need, None)
     assert rc == M.MOE_EINVAL  # workspace must be 256-byte aligned
+    rc = M.lib().moe_permute(ctypes.byref(desc), 64, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             need, None)
+    assert rc == M.MOE_EINVAL and "hidden" in M.moe_last_error()
+
 
 
 def test_shared_pointers_must_match_n_shared():

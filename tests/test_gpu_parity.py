@@ -73,6 +73,11 @@ def _small_cfg(name, idx, **kw):
     _small_cfg("E1_k1_dense", 5, E=1, k=1, n_shared=0, Fs=0, T=200),
     _small_cfg("k32_E64", 6, E=64, k=32, T=40),
     _small_cfg("wide_E1024", 7, E=1024, k=8, T=96, n_shared=0, Fs=0),
+    # small-T router and top-k with several router blocks, a partial last
+    # block, 16 top-k candidates a lane
+    _small_cfg("E48_T20", 36, E=48, k=6, T=20),
+    _small_cfg("E1024_T32", 37, E=1024, k=8, T=32, n_shared=0, Fs=0),
+    _small_cfg("E1000_T7_k32", 38, E=1000, k=32, T=7),
     _small_cfg("f32_ragged", 8, act=W.F32, router=W.F32, expert=W.F32, shared=W.F32, T=99,
                d=128, F=64, Fs=128),
     # b-bit group-32 routed experts (2, 3, 5, 6, 7, 8 bits), every tile size
@@ -343,7 +348,8 @@ def test_permute_against_oracle(n, E, skew):
     perm = torch.empty(n, dtype=torch.int32, device="cuda")
     inv = torch.empty(n, dtype=torch.int32, device="cuda")
     ws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
-    M.moe_permute(desc, n, k, ids_t, off, perm, inv, ws)
+    dummy_x = torch.zeros(16, dtype=torch.uint8, device="cuda")  # bf16 experts: not read
+    M.moe_permute(desc, n, k, dummy_x, ids_t, off, perm, inv, ws)
     torch.cuda.synchronize()
     o_off, o_perm, o_inv = oracle.route_plan(ids, E)
     assert np.array_equal(off.cpu().numpy(), o_off)
