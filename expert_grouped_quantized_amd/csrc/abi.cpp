@@ -81,6 +81,10 @@ moe_status check_tk(const moe_desc* D, int32_t T, int32_t k) {
     return fail(MOE_EINVAL, "k=%d outside [1, min(n_experts, %d)]", k, MAX_TOPK);
   if ((int64_t)T * k > (int64_t)1 << 30)
     return fail(MOE_EINVAL, "T*k=%lld exceeds 2^30", (long long)T * k);
+  // activation matrices (hidden, h) are addressed with 32-bit byte offsets
+  const int64_t wmax = std::max<int64_t>(D->ffn, D->n_shared ? D->shared_ffn : 0);
+  if ((int64_t)T * k * wmax >= (int64_t)1 << 31 || (int64_t)T * D->d >= (int64_t)1 << 31)
+    return fail(MOE_EINVAL, "T=%d, k=%d: T*k*ffn and T*d must stay below 2^31 elements", T, k);
   return MOE_OK;
 }
 

@@ -48,7 +48,8 @@ struct TileCtx {
   int run;              // this wave's run of 64 weight rows
   const uint8_t* sect;  // W1 or W2 section of this expert's blob
   const uint8_t* wt;    // this wave's run of weight tiles
-  const uint16_t* arow[3];
+  const uint8_t* abase; // activation rows (x, its fp16 copy, or h)
+  uint32_t aoff[3];     // byte offset of each staged piece's row and 16 bytes
 };
 
 // Lead of the loads, in K chunks: 4 for int4 and 2-bit codes (the bytes of the
@@ -77,9 +78,11 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
   // Chunk c of the activations travels in register set c % PF, then lands in
   // LDS buffer c & 1; chunk c of the weights sits in ring slot c % PF.
   u32x4_t areg[PF][PPT];
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(C.abase);
   auto load_a = [&](int kc, u32x4_t (&dst)[PPT]) {
+    const BufSrc src{arsrc, (uint32_t)(kc * KC * 2)};
 #pragma unroll
-    for (int j = 0; j < PPT; j++) dst[j] = *(const u32x4_t*)(C.arow[j] + kc * KC);
+    for (int j = 0; j < PPT; j++) dst[j] = src.ld16<false>(C.aoff[j]);
   };
   // Thread tid stages pieces (tid + 256 j) mod PIECES: in small tiles some
   // pieces are stored twice (same bytes, same place), so no store sits
@@ -122,13 +125,13 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
   // checks).
   static_assert(PF == 2 || PF == 4, "load lead must be 2 or 4 chunks");
   // stage 1: the caller issued the first PF weight chunks
-  const uint8_t* wnext = C.wt + (STAGE == 1 ? PF * tb : 0);
+  BufSrc wnext{buffer_rsrc(C.wt), (uint32_t)(STAGE == 1 ? PF * tb : 0)};
 #pragma unroll
   for (int p = 0; p < PF; p++) {
     load_a(p, areg[p]);
     if constexpr (STAGE != 1) {
       ring[p].template load<NT>(wnext, lane);
-      wnext += tb;
+      wnext.soff += (uint32_t)tb;
     }
   }
   store_a(sm.a[0], areg[0]);
@@ -145,7 +148,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       compute(sm.a[p & 1], ring[p]);
       if constexpr (MAXMF <= 2) __builtin_amdgcn_s_setprio(0);
       ring[p].template load<NT>(wnext, lane);
-      wnext += tb;
+      wnext.soff += (uint32_t)tb;
       store_a(sm.a[(p + 1) & 1], areg[(p + 1) % PF]);
       __syncthreads();
       // keep the scheduler from hoisting the next chunk's dequantization
@@ -177,7 +180,10 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
   constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
   constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
   static_assert(PPT <= 3, "A staging holds at most 3 pieces per thread");
-  const int tid = threadIdx.x, wave = tid >> 6;
+  // the wave index as a scalar: every weight address of the wave is then
+  // uniform (a scalar base plus the lane's offset), which keeps 64-bit
+  // per-lane pointers out of the vector registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   TileCtx C;
   C.Fw = J.shared ? A.Fs : A.F;
   const int K = STAGE == 1 ? A.d : C.Fw;
@@ -221,7 +227,8 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
   WTile<FMT> ring[PF];
   if constexpr (STAGE == 1) {
 #pragma unroll
-    for (int p = 0; p < PF; p++) ring[p].template load<NT>(C.wt + p * tb, tid & 63);
+    for (int p = 0; p < PF; p++)
+      ring[p].template load<NT>(BufSrc{buffer_rsrc(C.wt), (uint32_t)(p * tb)}, tid & 63);
   }
   if (m < ROWS) {
     sm.src[m] = src;
@@ -230,9 +237,12 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
   }
   __syncthreads();
 
-  const uint16_t* abase = STAGE == 1 ? (F16 ? (const uint16_t*)A.x16 : (const uint16_t*)A.hidden)
-                                     : (const uint16_t*)(J.shared ? A.h_shared : A.h_routed);
-  const size_t astride = STAGE == 1 ? (size_t)A.d : (size_t)C.Fw;
+  C.abase = STAGE == 1 ? (F16 ? (const uint8_t*)A.x16 : (const uint8_t*)A.hidden)
+                       : (const uint8_t*)(J.shared ? A.h_shared : A.h_routed);
+  // rows of 2-byte elements; every activation matrix is below 4 GiB (T*k <=
+  // 2^30 rows of <= 16384 columns would not be: the ABI bounds T*k*ffn and
+  // T*d to 2^31 elements)
+  const uint32_t astride = STAGE == 1 ? (uint32_t)A.d : (uint32_t)C.Fw;
   // Rows past the tile's end load the tile's first row: their accumulator
   // rows are never stored, and every lane issues the same loads.
 #pragma unroll
@@ -240,7 +250,7 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
     const int q = (tid + WAVES * 64 * j) % PIECES;  // piece q: row q / 8, 16-byte chunk q % 8
     const int r = q >> 3;
     const int s = sm.src[r] >= 0 ? sm.src[r] : sm.src[0];
-    C.arow[j] = abase + (size_t)s * astride + (q & 7) * 8;
+    C.aoff[j] = ((uint32_t)s * astride + (uint32_t)(q & 7) * 8) * 2;
   }
   tile_body<FMT, STAGE, MAXMF, PF_MAX, F16, NT>(A, J, sm, C, ring);
 }

@@ -29,6 +29,32 @@ __device__ __forceinline__ u32x4_t ldw(const uint8_t* base, int i) {
   return ((const u32x4_t*)base)[i];
 }
 
+// A stream of 16-byte loads addressed as a buffer: `rsrc` holds a scalar
+// base (a wave's run of weight tiles, or an activation matrix) and `soff` the
+// scalar byte offset of the current chunk, so a load takes only the lane's
+// 32-bit offset from a vector register -- no 64-bit per-lane address, and the
+// chunk advance is scalar arithmetic.  The whole 32-bit offset range is in
+// bounds (the ABI keeps every activation matrix below 4 GiB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff,
+                                           0x00020000);
+}
+struct BufSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t soff;
+  // NT: non-temporal (streamed past the caches)
+  template <bool NT>
+  __device__ __forceinline__ u32x4_t ld16(uint32_t voff) const {
+    return __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, NT ? 2 : 0));
+  }
+  template <bool NT>
+  __device__ __forceinline__ uint64_t ld8(uint32_t voff) const {
+    return __builtin_bit_cast(uint64_t,
+                              __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, NT ? 2 : 0));
+  }
+};
+
 // Constants of the int4 -> fp16 conversion, kept in registers (VOP3
 // encodings take no literal operands).
 struct F16Consts {
@@ -46,9 +72,9 @@ template <>
 struct WTile<MOE_BF16> {
   u32x4_t v[8];  // [frag][step]
   template <bool NT>
-  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+  __device__ __forceinline__ void load(const BufSrc& t, int lane) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = ldw<NT>(t, j * 64 + lane);
+    for (int j = 0; j < 8; j++) v[j] = t.ld16<NT>((uint32_t)(lane * 16 + j * 1024));
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
     return v[f * 2 + s];
@@ -66,10 +92,10 @@ struct WTile<MOE_I4_G32> {
   u32x4_t v[2];
   u32x4_t sc;  // 8 fp16 group scales, index f*2 + s (group = step)
   template <bool NT>
-  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
-    v[0] = ldw<NT>(t, lane);
-    v[1] = ldw<NT>(t, 64 + lane);
-    sc = ldw<NT>(t + 2048, lane & 15);
+  __device__ __forceinline__ void load(const BufSrc& t, int lane) {
+    v[0] = t.ld16<NT>((uint32_t)(lane * 16));
+    v[1] = t.ld16<NT>((uint32_t)(lane * 16 + 1024));
+    sc = t.ld16<NT>((uint32_t)((lane & 15) * 16 + 2048));
   }
   __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
     const int si = f * 2 + s;
@@ -125,9 +151,9 @@ template <>
 struct WTile<MOE_I8_ROW> {
   u32x4_t v[4];  // [frag]; dwords 2s, 2s+1 hold 8 int8 codes
   template <bool NT>
-  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+  __device__ __forceinline__ void load(const BufSrc& t, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) v[j] = ldw<NT>(t, j * 64 + lane);
+    for (int j = 0; j < 4; j++) v[j] = t.ld16<NT>((uint32_t)(lane * 16 + j * 1024));
   }
   __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
     const uint32_t w0 = v[f][2 * s], w1 = v[f][2 * s + 1];
@@ -173,21 +199,19 @@ struct WTileB {
   uint32_t w[NDW];
   u32x4_t sc;
   template <bool NT>
-  __device__ __forceinline__ void load(const uint8_t* t, int lane) {
+  __device__ __forceinline__ void load(const BufSrc& t, int lane) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
-      const u32x4_t v = ldw<NT>(t + g * 1024, lane);
+      const u32x4_t v = t.ld16<NT>((uint32_t)(g * 1024 + lane * 16));
 #pragma unroll
       for (int c = 0; c < 4; c++) w[4 * g + c] = v[c];
     }
     if constexpr (TAIL) {
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t* p = (const u32x2_t*)(t + G * 1024) + lane;
-      const u32x2_t v = NT ? __builtin_nontemporal_load(p) : *p;
-      w[4 * G] = v[0];
-      w[4 * G + 1] = v[1];
+      const uint64_t v = t.ld8<NT>((uint32_t)(G * 1024 + lane * 8));
+      w[4 * G] = (uint32_t)v;
+      w[4 * G + 1] = (uint32_t)(v >> 32);
     }
-    sc = ldw<NT>(t + 512 * B, lane & 15);
+    sc = t.ld16<NT>((uint32_t)(512 * B + (lane & 15) * 16));
   }
   __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
     const int si = f * 2 + s;

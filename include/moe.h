@@ -112,7 +112,8 @@ typedef enum moe_blob_kind {
  *   act MOE_BF16: expert_w MOE_BF16, MOE_I4_G32, MOE_I{2,3,5,6,7,8}_G32 or
  *                 MOE_MXFP4, shared_w MOE_BF16 or MOE_I8_ROW  (router bf16,
  *                 y bf16)
- * Sizes: 1 <= n_experts <= 1024; n_shared 0 or 1.  For act MOE_BF16:
+ * Sizes: 1 <= n_experts <= 1024; n_shared 0 or 1; every call needs
+ * T*k <= 2^30 and T*k*max(ffn, shared_ffn), T*d < 2^31.  For act MOE_BF16:
  * d % 256 == 0, ffn % 128 == 0 (% 256 with 2- or 4-bit or MXFP4 routed
  * weights), shared_ffn % 128 == 0.  For act MOE_F32:
  * d, ffn, shared_ffn multiples of 64.  d, ffn, shared_ffn <= 16384.         */
