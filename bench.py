@@ -38,12 +38,17 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
     p.add_argument("--workload", choices=("both", "prefill", "decode", "bits", "mxfp4", "configs"),
                    default="both",
-                   help="limit the run to one workload (for per-workload profiles)")
+                   help="limit the run to one workload (for per-workload profiles); the default "
+                        "runs the T=4096 prefill (headline), the T=16/32 decode and the other "
+                        "layer configurations")
+    p.add_argument("--no-configs", action="store_true",
+                   help="default run without the bf16 T=512, bf16-weight T=4096 and Zipf "
+                        "T=16384 layers")
     return p.parse_args()
 
 
@@ -438,12 +443,16 @@ def run_mxfp4(args, torch, W):
     return out
 
 
-def run_configs(args, torch, W):
+CPU_SAMPLE = {"bf16_T512": 512, "bf16w_T4096": 1024, "zipf_T16384": 2048}
+
+
+def run_configs(args, torch, W, with_cpu=False):
     """The layer configurations measured beside the headline ones, each as
     eager steps with the roofline its shape sits under: the bf16 layer at
     T=512 (weight bound: every expert's bf16 weights read once), the T=4096
     layer with bf16 routed weights (also weight bound), and T=16384 with int4
-    routed experts and Zipf-skewed routing (MFMA bound)."""
+    routed experts and Zipf-skewed routing (MFMA bound).  with_cpu: the oracle
+    timed on a token sample of each (CPU_SAMPLE tokens)."""
     import dataclasses
     cases = [("bf16_T512", W.CONFIGS["bf16_T512"], "hbm"),
              ("bf16w_T4096", dataclasses.replace(W.CONFIGS["int4_T4096"], name="bf16w_T4096",
@@ -469,6 +478,8 @@ def run_configs(args, torch, W):
                    ffn_gbs=A["ffn_bytes"] / ffn_s / 1e9,
                    ffn_hbm_frac=A["ffn_bytes"] / ffn_s / 1e9 / HBM_PEAK_GBS,
                    layer_hbm_frac=A["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        if with_cpu:
+            rec["cpu_baseline"] = cpu_baseline(cfg, S.inputs, cfg.T, CPU_SAMPLE[name])
         out[name] = rec
         print(f"[bench] {name}: {ms:.3f} ms/step (ffn {per[2]:.3f} ms, "
               f"{rec['ffn_tflops']:.0f} TFLOP/s, {rec['ffn_gbs']:.0f} GB/s)", file=sys.stderr,
@@ -538,16 +549,19 @@ def main():
                           "measured_peaks": peaks,
                           "mxfp4": _r(mx)}), flush=True)
         return
-    prefill = decode = roof_p = roof_d = pre_inputs = None
+    prefill = decode = roof_p = roof_d = pre_inputs = configs = None
     if args.workload in ("both", "prefill"):
         prefill, roof_p, pre_inputs = run_prefill(args, torch, W)
     if args.workload in ("both", "decode"):
         decode, roof_d = run_decode(args, torch, W)
-    peaks = measured_peaks(torch)
     cpu = None
     if not args.no_cpu_baseline and pre_inputs is not None:
         cfg = W.CONFIGS["int4_T4096"]
         cpu = cpu_baseline(cfg, pre_inputs, cfg.T, args.cpu_sample_tokens)
+        del pre_inputs
+    if args.workload == "both" and not args.no_configs:
+        configs = run_configs(args, torch, W, with_cpu=not args.no_cpu_baseline)
+    peaks = measured_peaks(torch)
 
     cfg = W.CONFIGS["int4_T4096"]
     common = {"d": cfg.d, "E": cfg.E, "k": cfg.k, "n_shared": cfg.n_shared, "F": cfg.F,
@@ -590,6 +604,8 @@ def main():
     if decode is not None:
         line["decode"] = _r(decode)
         line["decode_roofline"] = roof_d
+    if configs is not None:
+        line["configs"] = _r(configs)
     print(json.dumps(line, default=float), flush=True)
 
 
