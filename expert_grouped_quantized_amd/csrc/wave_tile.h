@@ -61,6 +61,17 @@ struct F16Consts {
   uint32_t lo, hi, magic;
 };
 
+// Group scale si (0..7) of the 8 fp16 scales in sc, in both halves of a
+// packed pair: the dword goes through a scalar (hipcc compiles a bit_cast of
+// an ext-vector element as a read of element 0), and the half is picked by a
+// shuffle that the packed multiply takes as its op_sel, one op fewer than an
+// integer splat.
+__device__ __forceinline__ f16x2_t scale_splat(const u32x4_t& sc, int si) {
+  const uint32_t dw = sc[si >> 1];
+  const f16x2_t p = __builtin_bit_cast(f16x2_t, dw);
+  return (si & 1) ? __builtin_shufflevector(p, p, 1, 1) : __builtin_shufflevector(p, p, 0, 0);
+}
+
 // ---- weight registers of one wave tile (64 rows x 64 K) -------------------
 // Fragment f (0..3) is 16 weight rows; step s (0..1) is 32 K.  Lane l holds
 // row l % 16 of each fragment and K elements 32*s + 8*(l/16) .. +7.
@@ -127,8 +138,7 @@ struct WTile<MOE_I4_G32> {
   // as 1024 + 16 (code + 8), and made exact with one packed fma by 1/16 and
   // -72 instead of a shift: one shift per dword instead of three.
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts& k) const {
-    const uint32_t sb = scale_bits(f, s);
-    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
+    const f16x2_t s2 = scale_splat(sc, f * 2 + s);
     const f16x2_t off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
@@ -228,6 +238,8 @@ struct WTileB {
   // reads as 1024 + code + 2^(b-1); one packed subtract makes the codes exact,
   // one packed multiply by the scale rounds each product to nearest even.
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
+    // integer splat of the scale: the op_sel form (scale_splat) makes the
+    // 96-row 2- and 7-bit gate/up kernels spill
     const uint32_t sb = scale_bits(f, s);
     const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
     constexpr _Float16 bias = (_Float16)(-(1024 + (1 << (B - 1))));
