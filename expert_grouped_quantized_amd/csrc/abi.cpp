@@ -166,14 +166,28 @@ struct OutIO {  // canonical outputs of unpacking
   uint8_t* s;
 };
 
-// b-bit group-32 tile: lane l's codes of fragment f, K step s, as one bit
-// stream (code + 2^(b-1) at bit (2f + s) 8b + i b for element i), then the
-// fp16 group scales [row c][f][s] at 512 b + c*16.
+// Position in lane l's stream of bit `k` of u = code + 2^(b-1), the offset
+// binary of element i (0..7) of fragment fi = 2 f + s.
+//   b = 2, 3 (bit planes, so the kernels cut out a pair of codes with one
+//   AND-OR): bits 0-1 in dword fi / 2 at 8 (fi % 2) + 16 (i % 2) + 2 (i / 2);
+//   b = 3's bit 2 in dword 4 + fi / 4 at 4 (fi % 4) + 16 (i % 2) + i / 2.
+//   b = 5..8: one little-endian stream, element i at bit fi 8 b + i b.
+inline int ig32_bit_pos(int b, int fi, int i, int k) {
+  if (b == 2 || b == 3) {
+    if (k < 2) return 32 * (fi >> 1) + 8 * (fi & 1) + 16 * (i & 1) + 2 * (i >> 1) + k;
+    return 32 * (4 + (fi >> 2)) + 4 * (fi & 3) + 16 * (i & 1) + (i >> 1);
+  }
+  return fi * 8 * b + i * b + k;
+}
+
+// b-bit group-32 tile: lane l's codes of fragment f, K step s, at the bit
+// positions of ig32_bit_pos, then the fp16 group scales [row c][f][s] at
+// 512 b + c*16.
 template <typename RowOf>
 int pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* dst) {
   const int b = ig32_bits(m[0]->fmt), lim = (1 << (b - 1)) - 1;
   for (int lane = 0; lane < 64; lane++) {
-    uint32_t w[17] = {0};  // one spare dword: a field may reach past the last
+    uint32_t w[16] = {0};
     for (int f = 0; f < 4; f++) {
       const MatIO& M = *m[f];
       const int64_t r = row_of(f, lane & 15);
@@ -182,12 +196,11 @@ int pack_tile_ig32(const MatIO* const m[4], RowOf row_of, int64_t kc, uint8_t* d
         for (int i = 0; i < 8; i++) {
           const int c = ((const int8_t*)M.q)[r * M.K + k0 + i];
           if (c < -lim || c > lim) return PK_CODE;
-          const uint64_t u = (uint64_t)(c + (1 << (b - 1)));
-          const int bit = (2 * f + s) * 8 * b + i * b;
-          const uint64_t cur = ((uint64_t)w[(bit >> 5) + 1] << 32) | w[bit >> 5];
-          const uint64_t nxt = cur | (u << (bit & 31));
-          w[bit >> 5] = (uint32_t)nxt;
-          w[(bit >> 5) + 1] = (uint32_t)(nxt >> 32);
+          const uint32_t u = (uint32_t)(c + (1 << (b - 1)));
+          for (int k = 0; k < b; k++) {
+            const int pos = ig32_bit_pos(b, 2 * f + s, i, k);
+            w[pos >> 5] |= ((u >> k) & 1u) << (pos & 31);
+          }
         }
       }
     }
@@ -271,16 +284,18 @@ void unpack_tile_ig32(const MatIO* const m[4], const OutIO out[4], RowOf row_of,
                       const uint8_t* src) {
   const int b = ig32_bits(m[0]->fmt);
   for (int lane = 0; lane < 64; lane++) {
-    uint32_t w[17] = {0};
+    uint32_t w[16] = {0};
     for (int dw = 0; dw < 2 * b; dw++) memcpy(&w[dw], src + ig32_dword_offset(b, lane, dw), 4);
     for (int f = 0; f < 4; f++) {
       const int64_t r = row_of(f, lane & 15), K = m[f]->K;
       for (int s = 0; s < 2; s++) {
         const int64_t k0 = kc * KC + s * 32 + 8 * (lane >> 4);
         for (int i = 0; i < 8; i++) {
-          const int bit = (2 * f + s) * 8 * b + i * b;
-          const uint64_t cur = ((uint64_t)w[(bit >> 5) + 1] << 32) | w[bit >> 5];
-          const int u = (int)((cur >> (bit & 31)) & ((1u << b) - 1));
+          int u = 0;
+          for (int k = 0; k < b; k++) {
+            const int pos = ig32_bit_pos(b, 2 * f + s, i, k);
+            u |= (int)((w[pos >> 5] >> (pos & 31)) & 1u) << k;
+          }
           ((int8_t*)out[f].q)[r * K + k0 + i] = (int8_t)(u - (1 << (b - 1)));
         }
       }

@@ -76,7 +76,8 @@ __host__ __device__ inline size_t tile_bytes(int fmt) {
 // K of one wave tile
 __host__ __device__ constexpr int kc_of(int fmt) { return fmt == MOE_MXFP4 ? KC_MX : KC; }
 // K chunks each wave keeps in flight for a weight format: 4- and 2-bit codes
-// take LEAD_I4, the other tiles LEAD_WIDE (their registers)
+// take LEAD_I4, the other tiles LEAD_WIDE (their registers; a lead of 4 for
+// 3-bit codes in the 16- and 32-row tiles measured slower at T=16)
 __host__ __device__ constexpr int lead_of(int fmt, int lead_i4) {
   return fmt == MOE_MXFP4 ? LEAD_MX
        : (ig32_bits(fmt) == 4 || ig32_bits(fmt) == 2) ? lead_i4 : LEAD_WIDE;

@@ -193,7 +193,7 @@ struct WTile<MOE_I8_ROW> {
   }
 };
 
-// ---- b-bit group-32 codes (b = 2, 3, 5, 6, 7, 8) ------------------------
+// ---- b-bit group-32 codes (b = 5, 6, 7, 8) ------------------------------
 // Lane l's codes of a wave tile form one little-endian bit stream of 64 b
 // bits: code i (0..7) of fragment f, K step s at bit (2 f + s) 8 b + i b, as
 // code + 2^(b-1) (offset binary).  The stream's dwords sit in 16-byte groups
@@ -269,8 +269,91 @@ struct WTileB {
     return r;
   }
 };
-template <> struct WTile<MOE_I2_G32> : WTileB<2> {};
-template <> struct WTile<MOE_I3_G32> : WTileB<3> {};
+// ---- 2- and 3-bit codes: bit planes laid out for pair extraction ---------
+// The low two bits of u = code + 2^(b-1) of element i (0..7) of fragment
+// fi = 2 f + s sit in stream dword fi / 2 at bit 8 (fi % 2) + 16 (i % 2) +
+// 2 (i / 2): the even elements in the low half, the odd ones in the high
+// half, so one AND-OR with 3 << 2j (in both halves) and the fp16 exponent of
+// 1024 gives the pair (2j, 2j+1) as two fp16 values 1024 + 4^j u2, exact.
+// For b = 3 the high bit of u sits in dword 4 + fi / 4 at bit 4 (fi % 4) +
+// 16 (i % 2) + i / 2 and reads as 1024 + 2^j u1 the same way.  Two (b = 2)
+// or three (b = 3) packed-fp16 ops per pair then make the codes exact, and
+// one packed multiply by the group scale rounds each product to nearest even
+// (fp16 MFMA); the bf16 form scales the exact codes in fp32 and rounds once
+// at the pack.  Group scales as in WTileB: [row c][f][s] at 512 b + c*16.
+template <int B>
+struct WTileP {
+  static_assert(B == 2 || B == 3, "bit-plane tiles hold 2- or 3-bit codes");
+  static constexpr int NDW = 2 * B;
+  uint32_t w[NDW];
+  u32x4_t sc;
+  template <bool NT>
+  __device__ __forceinline__ void load(const BufSrc& t, int lane) {
+    const u32x4_t v = t.ld16<NT>((uint32_t)(lane * 16));
+#pragma unroll
+    for (int c = 0; c < 4; c++) w[c] = v[c];
+    if constexpr (B == 3) {
+      const uint64_t h = t.ld8<NT>((uint32_t)(1024 + lane * 8));
+      w[4] = (uint32_t)h;
+      w[5] = (uint32_t)(h >> 32);
+    }
+    sc = t.ld16<NT>((uint32_t)(512 * B + (lane & 15) * 16));
+  }
+  __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
+    const int si = f * 2 + s;
+    const uint32_t sw = sc[si >> 1];
+    return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
+  }
+  // the 4 exact code pairs of fragment (f, s), as packed fp16
+  __device__ __forceinline__ void codes(int f, int s, f16x2_t (&c)[4]) const {
+    const int fi = 2 * f + s;
+    const uint32_t q2 = (fi & 1) ? w[fi >> 1] >> 8 : w[fi >> 1];
+    uint32_t q1 = 0;
+    if constexpr (B == 3) q1 = w[4 + (fi >> 2)] >> (4 * (fi & 3));
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f16x2_t t2 =
+          __builtin_bit_cast(f16x2_t, and_or_b32(q2, 0x00030003u << (2 * j), 0x64006400u));
+      // 4^-j scales the low plane down to 1024 4^-j + u2
+      const _Float16 k2 = (_Float16)(1.0f / (float)(1 << (2 * j)));
+      if constexpr (B == 2) {
+        const _Float16 o = (_Float16)(-(1024.0f / (float)(1 << (2 * j)) + 2.0f));
+        c[j] = t2 * f16x2_t{k2, k2} + f16x2_t{o, o};
+      } else {
+        const f16x2_t t1 =
+            __builtin_bit_cast(f16x2_t, and_or_b32(q1, 0x00010001u << j, 0x64006400u));
+        // 4 u1 - 1024 4^-j - 4, exact: t1 (4 2^-j) = 4096 2^-j + 4 u1
+        const _Float16 k1 = (_Float16)(4.0f / (float)(1 << j));
+        const _Float16 o = (_Float16)(-(4096.0f / (float)(1 << j) + 1024.0f / (float)(1 << (2 * j)) +
+                                        4.0f));
+        c[j] = t2 * f16x2_t{k2, k2} + (t1 * f16x2_t{k1, k1} + f16x2_t{o, o});
+      }
+    }
+  }
+  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
+    const f16x2_t s2 = scale_splat(sc, f * 2 + s);
+    f16x2_t c[4];
+    codes(f, s, c);
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f16x2_t p = c[j] * s2;
+      r[j] = __builtin_bit_cast(uint32_t, p);
+    }
+    return r;
+  }
+  __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
+    const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
+    f16x2_t c[4];
+    codes(f, s, c);
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; j++) r[j] = pack_bf16x2((float)c[j][0] * scale, (float)c[j][1] * scale);
+    return r;
+  }
+};
+template <> struct WTile<MOE_I2_G32> : WTileP<2> {};
+template <> struct WTile<MOE_I3_G32> : WTileP<3> {};
 template <> struct WTile<MOE_I5_G32> : WTileB<5> {};
 template <> struct WTile<MOE_I6_G32> : WTileB<6> {};
 template <> struct WTile<MOE_I7_G32> : WTileB<7> {};

@@ -16,8 +16,8 @@ import re
 import pytest
 
 CSRC = os.path.join(os.path.dirname(__file__), "..", "expert_grouped_quantized_amd", "csrc")
-# a bit_cast whose operand is an indexed element: bit_cast(T, name[...])
-ELEMENT_CAST = re.compile(r"__builtin_bit_cast\(\s*[\w:<> ]+,\s*[\w.>-]+\s*\[")
+# a bit_cast whose whole operand is an indexed element: bit_cast(T, name[...])
+ELEMENT_CAST = re.compile(r"__builtin_bit_cast\(\s*[\w:<> ]+,\s*[\w.>-]+\s*\[[^\]]*\]\s*\)")
 
 
 def _sources():
@@ -40,6 +40,7 @@ def test_no_bit_cast_of_an_indexed_element():
     ("const f16x2_t t = __builtin_bit_cast(f16x2_t, sc[si >> 1]);", True),
     ("const uint32_t e = v[w]; x = __builtin_bit_cast(f16x2_t, e);", False),
     ("r[j] = __builtin_bit_cast(uint32_t, (t0 + off) * s2);", False),
+    ("r[j] = __builtin_bit_cast(uint32_t, c[j] * s2);", False),
 ])
 def test_the_pattern_itself(line, flagged):
     assert bool(ELEMENT_CAST.search(line)) == flagged
