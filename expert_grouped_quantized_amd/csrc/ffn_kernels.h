@@ -34,9 +34,12 @@ struct TileJob {
   int expert, start, cnt, nb;
 };
 
-template <int MAXMF>
+// SLOTS: A chunks held in LDS -- 4 for tiles with a 4-chunk load lead (two
+// chunks are read while the next two are written, one barrier per two
+// chunks), 2 otherwise.
+template <int MAXMF, int SLOTS = 2>
 struct Smem {
-  uint16_t a[2][MAXMF * 16 * 64];
+  uint16_t a[SLOTS][MAXMF * 16 * 64];
   float wrow[MAXMF * 16];
   float xs[MAXMF * 16];  // power of two to undo on fp16-staged rows
   int src[MAXMF * 16];
@@ -56,8 +59,12 @@ struct TileCtx {
 // call); 2 for bf16 tiles (4x the bytes and registers of an int4 tile), int8
 // shared tiles (re-read from cache by every row tile) and the 3- and 5- to
 // 8-bit codes (their registers).
+template <int FMT, int PF_MAX>
+constexpr int slots_of() { return lead_of(FMT, PF_MAX) == 4 ? 4 : 2; }
+
 template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
-__device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm,
+__device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J,
+                                          Smem<MAXMF, slots_of<FMT, PF_MAX>()>& sm,
                                           const TileCtx& C,
                                           WTile<FMT> (&ring)[lead_of(FMT, PF_MAX)]) {
   constexpr int NMF = MAXMF;
@@ -134,6 +141,36 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       wnext.soff += (uint32_t)tb;
     }
   }
+  if constexpr (PF == 4) {
+    // Four LDS slots: step c computes chunk c from slot c % 4 and stores
+    // chunk c + 2 into slot (c + 2) % 4, whose chunk c - 2 every wave read
+    // before the last barrier; a barrier after every second step publishes
+    // the two chunks stored since the previous one.  A chunk's activations
+    // wait two steps in registers between load and store.
+    store_a(sm.a[0], areg[0]);
+    store_a(sm.a[1], areg[1]);
+    __syncthreads();
+    for (int kc0 = 0; kc0 < nk - PF; kc0 += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; p++) {
+        load_a(kc0 + p + PF, areg[p]);  // set p held chunk kc0 + p, stored two steps ago
+        if constexpr (MAXMF <= 2) __builtin_amdgcn_s_setprio(1);
+        compute(sm.a[p], ring[p]);
+        if constexpr (MAXMF <= 2) __builtin_amdgcn_s_setprio(0);
+        ring[p].template load<NT>(wnext, lane);
+        wnext.soff += (uint32_t)tb;
+        store_a(sm.a[(p + 2) % 4], areg[(p + 2) % PF]);
+        if (p & 1) __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; p++) {  // the last PF chunks: nothing more to load
+      compute(sm.a[p], ring[p]);
+      if (p < 2) store_a(sm.a[p + 2], areg[p + 2]);
+      if (p == 1) __syncthreads();
+    }
+  } else {
   store_a(sm.a[0], areg[0]);
   __syncthreads();
   for (int kc0 = 0; kc0 < nk - PF; kc0 += PF) {
@@ -164,6 +201,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
       __syncthreads();
     }
   }
+  }
 
   const int quad = 4 * (lane >> 4);
   store_wave_tile<FMT, STAGE, NMF, F16>(
@@ -175,7 +213,8 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J, Sm
 // F16: stage-1 tile on fp16 MFMA, A rows from the fp16 copy of the
 // activations (scaled per token by a power of two, undone in the epilogue).
 template <int FMT, int STAGE, int MAXMF, int PF_MAX, bool F16, bool NT>
-__device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Smem<MAXMF>& sm) {
+__device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J,
+                                         Smem<MAXMF, slots_of<FMT, PF_MAX>()>& sm) {
   constexpr int ROWS = MAXMF * 16;
   constexpr int PIECES = ROWS * 8;  // 16-byte pieces of one A chunk
   constexpr int PPT = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
@@ -263,14 +302,15 @@ __device__ __forceinline__ void run_tile(const FfnArgs& A, const TileJob& J, Sme
 // rows; experts spilling past 96 rows leave small second tiles).
 template <int RF, int STAGE, int MAXMF, int PF, bool F16, bool NT>
 __device__ __forceinline__ void run_routed_tile(const FfnArgs& A, const TileJob& J,
-                                                Smem<MAXMF>& sm) {
+                                                Smem<MAXMF, slots_of<RF, PF>()>& sm) {
+  constexpr int SL = slots_of<RF, PF>();
   if constexpr (MAXMF == 6) {
     if (J.cnt <= 32)
-      return run_tile<RF, STAGE, 2, PF, F16, NT>(A, J, *reinterpret_cast<Smem<2>*>(&sm));
+      return run_tile<RF, STAGE, 2, PF, F16, NT>(A, J, *reinterpret_cast<Smem<2, SL>*>(&sm));
     if (J.cnt <= 64)
-      return run_tile<RF, STAGE, 4, PF, F16, NT>(A, J, *reinterpret_cast<Smem<4>*>(&sm));
+      return run_tile<RF, STAGE, 4, PF, F16, NT>(A, J, *reinterpret_cast<Smem<4, SL>*>(&sm));
     if (J.cnt <= 80)
-      return run_tile<RF, STAGE, 5, PF, F16, NT>(A, J, *reinterpret_cast<Smem<5>*>(&sm));
+      return run_tile<RF, STAGE, 5, PF, F16, NT>(A, J, *reinterpret_cast<Smem<5, SL>*>(&sm));
   }
   run_tile<RF, STAGE, MAXMF, PF, F16, NT>(A, J, sm);
 }
@@ -330,7 +370,7 @@ __host__ __device__ __forceinline__ int col_blocks(int runs) { return (runs + WA
 
 template <int RF, int SF, int STAGE, int MAXMF, int PF, bool NT_ROUTED>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
-  __shared__ __attribute__((aligned(16))) Smem<MAXMF> sm;
+  __shared__ __attribute__((aligned(16))) Smem<MAXMF, slots_of<RF, PF>()> sm;
   const int nr = STAGE == 1 ? col_blocks(A.F / H_COLS_WAVE) : col_blocks(A.d / OUT_COLS_WAVE);
   const int ns = STAGE == 1 ? (A.n_shared ? col_blocks(A.Fs / H_COLS_WAVE) : 0) : nr;
   TileJob J;
@@ -342,8 +382,10 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void ffn_kernel(FfnArgs A) {
   // shared expert's weights are re-read by every row tile: those stay
   // cacheable.
   constexpr bool NT_SHARED = false;
+  static_assert(slots_of<SF, PF>() <= slots_of<RF, PF>(), "shared tiles fit the routed LDS");
   if (J.shared)
-    run_tile<SF, STAGE, MAXMF, PF, STAGE == 1 && X16 && SF == MOE_I8_ROW, NT_SHARED>(A, J, sm);
+    run_tile<SF, STAGE, MAXMF, PF, STAGE == 1 && X16 && SF == MOE_I8_ROW, NT_SHARED>(
+        A, J, *reinterpret_cast<Smem<MAXMF, slots_of<SF, PF>()>*>(&sm));
   else
     run_routed_tile<RF, STAGE, MAXMF, PF, STAGE == 1 && X16, NT_ROUTED>(A, J, sm);
 }
