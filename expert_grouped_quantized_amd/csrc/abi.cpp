@@ -100,11 +100,9 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
     if (_s != MOE_OK) return _s;    \
   } while (0)
 
-// Calls of at most 32 tokens on int4 / b-bit layers get the fp16 copy of x
-// (and its per-token scales) from the route plan's launch.
-bool small_call_x16(const moe_desc* D, int32_t T) {
-  return D->act == MOE_BF16 && ig32_bits(D->expert_w) != 0 && tile_rows(T) != BM;
-}
+// int4 / b-bit layers get the fp16 copy of x (and its per-token scales) from
+// the route plan's first launch.
+bool x16_layer(const moe_desc* D) { return D->act == MOE_BF16 && ig32_bits(D->expert_w) != 0; }
 
 moe_status device_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MOE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -567,7 +565,7 @@ moe_status moe::grouped_ffn_call(const moe_desc* D, int32_t T, int32_t k, const 
   if (scratch) {
     const hipError_t e = launch_tiles_from_offsets(
         D->n_experts, tile_rows(T), L.routed_slots, offsets, (int4*)(w + L.tiles), T, D->d,
-        small_call_x16(D, T) ? (const uint16_t*)hidden : nullptr, a.x16, a.xscale, s);
+        x16_layer(D) ? (const uint16_t*)hidden : nullptr, a.x16, a.xscale, s);
     if (e != hipSuccess) return device_result(e, "row-tile plan launch");
   }
   return device_result(D->act == MOE_F32 ? launch_ffn_f32(a, s) : launch_ffn_bf16(a, s),
@@ -673,7 +671,7 @@ moe_status moe_permute(const moe_desc* D, int32_t T, int32_t k, const void* hidd
   if (ws_bytes < L.total)
     return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if (T == 0) return ok();
-  const uint16_t* xs = small_call_x16(D, T) ? (const uint16_t*)hidden : nullptr;
+  const uint16_t* xs = x16_layer(D) ? (const uint16_t*)hidden : nullptr;
   return device_result(launch_plan(T, k, D->n_experts, tile_rows(T), topk_ids, offsets, perm,
                                    inv_perm, workspace, L, D->d, xs, (hipStream_t)stream),
                        "route-plan launch");

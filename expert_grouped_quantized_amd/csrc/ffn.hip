@@ -1,28 +1,9 @@
 // ffn.hip -- launches of the expert-grouped SwiGLU GEMMs for bf16 and int4
-// routed weights (other code widths: ffn_lowbit.hip; MXFP4: ffn_mx.hip), the
-// fp16 activation copy of int4 and b-bit layers, and the fp32 path.
+// routed weights (other code widths: ffn_lowbit.hip; MXFP4: ffn_mx.hip) and
+// the fp32 path.
 #include "ffn_kernels.h"
 
 namespace moe {
-
-// Activations of an int4 layer as fp16 (calls of more than 32 tokens): each
-// token row scaled by 2^-e (row_fp16_exponent), 2^e kept for the gate/up
-// epilogue; one wave per row.  (For calls of at most 32 tokens moe_permute's
-// plan launch writes the same copy from blocks of its own.)
-__global__ __launch_bounds__(256) void x_to_f16_kernel(int T, int d, const uint16_t* __restrict__ x,
-                                                       uint16_t* __restrict__ x16,
-                                                       float* __restrict__ xscale) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  wave_row_to_f16(t, d, x, x16, xscale);
-}
-
-hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s) {
-  x_to_f16_kernel<<<(a.T + 3) / 4, 256, 0, s>>>(a.T, a.d, (const uint16_t*)a.hidden, a.x16,
-                                                 a.xscale);
-  return hipGetLastError();
-}
-
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   const int sf = a.n_shared ? a.shared_fmt : MOE_BF16;

@@ -401,12 +401,7 @@ static hipError_t launch_stages(const FfnArgs& a0, hipStream_t s) {
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
   const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
   const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
-  // calls of at most 32 tokens get their fp16 copy of x from moe_permute's
-  // plan launch (one launch fewer on the decode path)
-  if (x16_path(RF, MAXMF) && MAXMF > 2) {
-    hipError_t e = launch_x_to_f16(a, s);
-    if (e != hipSuccess) return e;
-  }
+  // the fp16 copy of x of int4 / b-bit layers comes from moe_permute's plan
   ffn_kernel<RF, SF, 1, MAXMF, PF, NT_ROUTED><<<slots * nb1, WAVES * 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -111,8 +111,8 @@ struct WsLayout {
                        //   (MXFP4 layers: e2m1 codes [T*k, F/2], chunk-major)
   size_t h_scale;      // MXFP4 layers: E8M0 [T*k, F/32], the scales of h
   size_t h_shared;     // act-typed [T, Fs]     intermediate h of the shared expert
-  size_t x16;          // fp16 [T, d]           activations scaled by 2^-xexp[t] (int4 path;
-                       //                       written by moe_permute at T <= 32)
+  size_t x16;          // fp16 [T, d]           activations scaled by 2^-xexp[t] (int4 / b-bit
+                       //                       layers; written by moe_permute)
                        //   (MXFP4 layers: e2m1 codes of x in plan order [T*k, d/2])
   size_t xexp;         // float [T]             2^xexp[t], the scale to undo
                        //   (MXFP4 layers: E8M0 [T*k, d/32], the scales of x)
@@ -150,9 +150,9 @@ hipError_t launch_router_f32(int T, int d, int E, const float* x, const float* w
                              const float* bias, float* logits, hipStream_t s);
 hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w,
                        hipStream_t s);
-// Route plan of T*k ids, tiles of `rows` rows.  x_for_f16 (one-chunk plans
-// only, else NULL): also write the fp16 copy of x (rows of d) and its
-// per-token scales into the workspace, as x_to_f16 would.
+// Route plan of T*k ids, tiles of `rows` rows.  x_for_f16 (int4 / b-bit
+// layers, else NULL): also write the fp16 copy of x (rows of d, each scaled
+// by a power of two) and its per-token scales into the workspace.
 hipError_t launch_plan(int T, int k, int E, int rows, const int32_t* ids, int32_t* offsets,
                        int32_t* perm, int32_t* inv_perm, void* ws, const WsLayout& L, int d,
                        const uint16_t* x_for_f16, hipStream_t s);
@@ -187,8 +187,6 @@ hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_lowbit(const FfnArgs& a, hipStream_t s);
 // MXFP4 W4A4 routed experts
 hipError_t launch_ffn_mx(const FfnArgs& a, hipStream_t s);
-// x -> fp16 copy and per-token scale (int4 layers)
-hipError_t launch_x_to_f16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int act, const float* out_assign,
                           const int32_t* inv_perm, const float* shared_out, void* y,
                           hipStream_t s);

@@ -14,16 +14,36 @@
 //                  (lanes holding the same expert id) plus per-wave counts in
 //                  LDS; perm/inv_perm scattered; chunk 0 also writes offsets
 //                  and the row-tile plan for the grouped GEMMs.
+// For int4 / b-bit layers the first launch also carries blocks that write the
+// fp16 copy of x the grouped gate/up products run on (see x16_blocks).
 // Only the histogram uses atomics, and counts do not depend on their order;
 // every position is a function of the input alone.
 #include "plan_kernels.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(PLAN_THREADS) void plan_count_kernel(int n, int E,
-                                                                  const int32_t* __restrict__ ids,
-                                                                  int32_t* __restrict__ counts) {
+// Blocks past the plan's own that write the fp16 copy of an int4 (or b-bit)
+// layer's activations and its per-token scales (x given): one wave per token.
+// They share the plan's first launch (they need nothing from it), so the copy
+// costs no launch of its own and runs beside the histogram.
+constexpr int X16_TOKENS_PER_BLOCK = PLAN_THREADS / 64;
+inline int x16_blocks(int T, const uint16_t* x) {
+  return x ? (T + X16_TOKENS_PER_BLOCK - 1) / X16_TOKENS_PER_BLOCK : 0;
+}
+
+// Blocks 0 .. n_chunks-1: one chunk's histogram each; blocks past them: the
+// fp16 copy of x (x given).
+__global__ __launch_bounds__(PLAN_THREADS) void plan_count_kernel(
+    int n, int E, int n_chunks, const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
+    int T, int d, const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
+    float* __restrict__ xscale) {
   __shared__ int hist[MAX_EXPERTS];
+  if ((int)blockIdx.x >= n_chunks) {
+    rows_to_f16(T, d, x, x16, xscale,
+                ((int)blockIdx.x - n_chunks) * X16_TOKENS_PER_BLOCK + (threadIdx.x >> 6),
+                ((int)gridDim.x - n_chunks) * X16_TOKENS_PER_BLOCK);
+    return;
+  }
   const int tid = threadIdx.x, base = blockIdx.x * PLAN_CHUNK;
   const int len = min(PLAN_CHUNK, n - base);
   for (int e = tid; e < E; e += PLAN_THREADS) hist[e] = 0;
@@ -33,14 +53,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_count_kernel(int n, int E,
   for (int e = tid; e < E; e += PLAN_THREADS) counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Blocks past the plan's own that write the fp16 copy of an int4 (or b-bit)
-// layer's activations and its per-token scales (the work of x_to_f16_kernel)
-// for calls of at most 32 tokens, saving the decode path a launch: one wave
-// per token.
-constexpr int X16_TOKENS_PER_BLOCK = PLAN_THREADS / 64;
-inline int x16_blocks(int T, const uint16_t* x) {
-  return x ? (T + X16_TOKENS_PER_BLOCK - 1) / X16_TOKENS_PER_BLOCK : 0;
-}
 
 // The row tiles alone, from a finished plan's offsets (block 0), and the
 // fp16 copy of x (blocks past it, when x is given).
@@ -69,8 +81,8 @@ hipError_t launch_tiles_from_offsets(int E, int rows, int slots, const int32_t* 
   return hipGetLastError();
 }
 
-// One chunk per block.  A one-chunk plan may carry extra blocks that write
-// the fp16 copy of x (x given; see x16_blocks).
+// One chunk per block.  A one-chunk plan (the only launch of its plan) may
+// carry the blocks that write the fp16 copy of x (x given; see x16_blocks).
 template <bool SINGLE>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     int n, int E, int n_chunks, const int32_t* __restrict__ ids,
@@ -102,8 +114,8 @@ hipError_t launch_plan(int T, int k, int E, int rows, const int32_t* ids, int32_
         n, E, 1, ids, counts, offsets, perm, inv_perm, rows, L.routed_slots, tiles, T, d,
         x_for_f16, x16, xscale);
   } else {
-    if (x_for_f16) return hipErrorInvalidValue;  // the copy rides on one-chunk (small) plans
-    plan_count_kernel<<<L.n_chunks, PLAN_THREADS, 0, s>>>(n, E, ids, counts);
+    plan_count_kernel<<<L.n_chunks + x16_blocks(T, x_for_f16), PLAN_THREADS, 0, s>>>(
+        n, E, L.n_chunks, ids, counts, T, d, x_for_f16, x16, xscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     plan_scatter_kernel<false><<<L.n_chunks, PLAN_THREADS, 0, s>>>(

@@ -196,7 +196,7 @@ moe_status moe_route_from_logits(const moe_desc* desc, int32_t T, int32_t k, con
 /* Route plan ("Dedicated prefill lane", step 1): the assignments ordered by
  * expert, the same order on every run.
  *   hidden    [T, d] act dtype, the layer's input (read only by int4 and b-bit
- *             layers at T <= 32: see workspace)
+ *             layers: see workspace)
  *   topk_ids  [T*k] int32, flat index f = t*k + s, values in [0, E)
  *   offsets   [E+1] int32 out: offsets[e] = #{f : ids[f] < e}; offsets[E] = T*k
  *   perm      [T*k] int32 out: the f of expert e, ascending, at
@@ -204,10 +204,9 @@ moe_status moe_route_from_logits(const moe_desc* desc, int32_t T, int32_t k, con
  *   inv_perm  [T*k] int32 out: inv_perm[perm[p]] = p
  *   workspace scratch of >= moe_workspace_bytes(desc, T, k); this call also
  *             leaves in it what moe_grouped_ffn reads besides its arguments --
- *             the row-tile plan, and for int4 / b-bit layers at T <= 32 the
- *             fp16 copy of hidden that their gate/up products run on (each
- *             token row scaled by a power of two; moe_grouped_ffn makes it
- *             itself at larger T) -- so pass the same workspace, unchanged,
+ *             the row-tile plan, and for int4 / b-bit layers the fp16 copy
+ *             of hidden that their gate/up products run on (each token row
+ *             scaled by a power of two) -- so pass the same workspace, unchanged,
  *             and the same hidden to the moe_grouped_ffn call that consumes
  *             this plan.                                                   */
 moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,

@@ -36,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # dispatches with the largest / smallest grid (x quantization runs for every
 # call size in the same process)
 FFN_KERNELS = {
-    "prefill": [(r"ffn_kernel<2, 3, [12], 6, 4, (true|false)>", "all"), (r"x_to_f16_kernel", "all")],
+    "prefill": [(r"ffn_kernel<2, 3, [12], 6, 4, (true|false)>", "all")],
     "decode": [(r"ffn_kernel<2, 3, [12], 1, 4, (true|false)>", "all")],
     "mxfp4_prefill": [(r"ffn_mx_kernel<3, [12], 6, 2>", "all"), (r"x_to_mx_kernel", "largest")],
     "mxfp4_decode": [(r"ffn_mx_kernel<3, [12], 1, 2>", "all"), (r"x_to_mx_kernel", "smallest")],

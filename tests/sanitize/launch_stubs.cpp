@@ -27,7 +27,6 @@ hipError_t launch_ffn_bf16(const FfnArgs&, hipStream_t) { return hipErrorNoDevic
 hipError_t launch_ffn_f32(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_ffn_lowbit(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_ffn_mx(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_x_to_f16(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_combine(int, int, int, int, const float*, const int32_t*, const float*, void*,
                           hipStream_t) {
   return hipErrorNoDevice;
