@@ -101,7 +101,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& A, const TileJob& J,
       *(u32x4_t*)(dst + lds_a_index(q >> 3, q & 7)) = src[j];
     }
   };
-  const F16Consts f16k = {0x000f000fu, 0x00f000f0u, 0x64006400u};
+  const F16Consts f16k = {0x000f000fu, 0x00f000f0u, 0x64006400u, 0x54005400u};
   // One chunk on all MAXMF row fragments.  Fragments past the tile's last row
   // hold copies of its first row and are never stored: a straight-line run of
   // MFMAs with no branch beats skipping them (a scalar branch per fragment

@@ -56,9 +56,10 @@ struct BufSrc {
 };
 
 // Constants of the int4 -> fp16 conversion, kept in registers (VOP3
-// encodings take no literal operands).
+// encodings take no literal operands): the low- and high-nibble masks of a
+// pair and the fp16 exponents of 1024 and 64 in both halves.
 struct F16Consts {
-  uint32_t lo, hi, magic;
+  uint32_t lo, hi, magic, magic64;
 };
 
 // Group scale si (0..7) of the 8 fp16 scales in sc, in both halves of a
@@ -116,18 +117,27 @@ struct WTile<MOE_I4_G32> {
   // bf16(code * scale): a nibble pair OR-ed under the fp16 exponent of 1024
   // reads as 1024 + code + 8 each; one mixed-precision FMA per half takes it
   // with the fp16 scale and -1032 * scale (both products exact in fp32, so the
-  // sum is code * scale exactly) and the pack rounds to nearest even.  Two
-  // VALU ops per nibble pair fewer than a byte convert per code.
+  // sum is code * scale exactly) and the pack rounds to nearest even.  The
+  // pairs in the high nibbles of bytes 0 and 2 are taken in place under the
+  // exponent of 64, where those bits count 1 to 8: 64 + code + 8, made exact
+  // with -72 * scale, so one shift per dword serves all four pairs.  Both
+  // biases are mixed-precision FMAs of the fp16 scale (no conversion).
   __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts& k) const {
     const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)scale_bits(f, s));
     const float scale = (float)sh;
-    const float bias = -1032.0f * scale;
+    const float bias_lo = fmaf((float)sh, -1032.0f, 0.0f);
+    const float bias_hi = fmaf((float)sh, -72.0f, 0.0f);
     const uint32_t q = v[f >> 1][(f & 1) * 2 + s];
+    const uint32_t q8 = q >> 8;
+    const uint32_t w[4] = {and_or_b32(q, k.lo, k.magic), and_or_b32(q, k.hi, k.magic64),
+                           and_or_b32(q8, k.lo, k.magic), and_or_b32(q8, k.hi, k.magic64)};
     u32x4_t r;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const f16x2_t t = __builtin_bit_cast(f16x2_t, and_or_b32(q >> (4 * j), k.lo, k.magic));
-      r[j] = pack_bf16x2(fmaf((float)t[0], scale, bias), fmaf((float)t[1], scale, bias));
+      const uint32_t wj = w[j];
+      const f16x2_t t = __builtin_bit_cast(f16x2_t, wj);
+      const float b = (j & 1) ? bias_hi : bias_lo;
+      r[j] = pack_bf16x2(fmaf((float)t[0], scale, b), fmaf((float)t[1], scale, b));
     }
     return r;
   }
