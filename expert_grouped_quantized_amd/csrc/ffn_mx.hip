@@ -4,9 +4,8 @@
 // expert 16-bit), in the OCP Microscaling FP4 format that CDNA4's scaled
 // MFMA (16x16x128, e2m1 operands, one E8M0 scale per 32 K per row) consumes.
 //
-//   x_to_mx_kernel   x, gathered into route-plan order (row p = token
-//                    perm[p] / k) -> e2m1 codes + E8M0 scales, block by block
-//                    of 32 (OCP MX rule), into the workspace
+//   x_to_mx_kernel   x -> e2m1 codes + E8M0 scales, block by block of 32
+//                    (OCP MX rule), one row per token, into the workspace
 //   ffn_mx_kernel<1> routed tiles: g, u = Wg xq, Wu xq on the FP4 MFMA;
 //                    h = w * silu(g) * u in fp32, quantized per row and 32 h
 //                    columns (one wave's columns) -> hq, hsc
@@ -22,9 +21,9 @@
 // through LDS, double-buffered.  No dequantization: codes and scales feed the
 // MFMA as they are.
 //
-// Activation layout (x's codes and h's codes, both in route-plan row order,
-// n = T*k rows): chunk-major, so the rows of a tile are contiguous in every
-// 128-K chunk --
+// Activation layout, chunk-major (x's codes: n = T rows in token order, which
+// the gate/up tiles gather through perm while staging; h's codes: n = T*k
+// rows in route-plan order, so the rows of a down tile are contiguous) --
 //   codes   q[(kc * n + p) * 64 + kb * 16 + j]   chunk kc, row p, 32-K block kb
 //   scales  s[((kc / 2) * n + p) * 8 + (kc % 2) * 4 + kb]   (pairs of chunks)
 // The gate/up epilogue of column block nb writes chunk nb of h (its 128 h
@@ -78,23 +77,21 @@ __device__ __forceinline__ int mx_exponent(uint32_t amax_bits, float* inv) {
 
 // ---- x -> MXFP4 --------------------------------------------------------------
 // One thread per 32-element block: thread g takes block kb = g % 4 of chunk kc
-// of plan row p ((g / 4) = kc * n + p), so four threads read 256 contiguous
-// bytes of the token's row and write one row's 64 code bytes, and successive
-// rows follow each other in the output.  A token's row is quantized once per
-// assignment (k times), to the same codes.
-__global__ __launch_bounds__(256) void x_to_mx_kernel(int n, int k, int d,
-                                                      const uint16_t* __restrict__ x,
-                                                      const int32_t* __restrict__ perm,
+// of token t ((g / 4) = kc * n + t, n = T), so four threads read 256
+// contiguous bytes of the token's row and write one row's 64 code bytes, and
+// successive rows follow each other in the output.  Each token is quantized
+// once; its k assignments' tiles gather its codes.
+__global__ __launch_bounds__(256) void x_to_mx_kernel(int n, int d, const uint16_t* __restrict__ x,
                                                       uint8_t* __restrict__ xq,
                                                       uint8_t* __restrict__ xsc) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t nblk = (int64_t)n * (d / 32);
   if (g >= nblk) return;
   const int kb = (int)(g & 3);
-  const int64_t cp = g >> 2;  // kc * n + p
+  const int64_t cp = g >> 2;  // kc * n + t
   const int kc = (int)(cp / n);
-  const int p = (int)(cp - (int64_t)kc * n);
-  const int64_t t = perm[p] / k;
+  const int64_t t = cp - (int64_t)kc * n;
+  const int p = (int)t;
   const u32x4_t* src = (const u32x4_t*)(x + t * d + (kc * 4 + kb) * 32);
   u32x4_t v[4];
 #pragma unroll
@@ -150,6 +147,7 @@ struct SmemMx {
   uint8_t a[2][MAXMF * 16 * 64];
   uint8_t s[2][4 * 16 * 8];
   float wrow[MAXMF * 16];
+  int src[MAXMF * 16];  // A row of each tile row (gate/up: its token)
 };
 
 // Stage-1 epilogue: h = w * silu(g) * u of the wave's 32 h columns, quantized
@@ -242,30 +240,39 @@ __device__ __forceinline__ void run_tile_mx(const FfnArgs& A, const TileJob& J, 
   const uint8_t* sect = STAGE == 1 ? blob : blob + w1_bytes(MOE_MXFP4, A.d, A.F);
   const uint8_t* wnext = sect + (size_t)run * nk * TILE_BYTES_MX4;
 
-  // folded router weight of each tile row (gate/up)
-  for (int m = tid; m < ROWS; m += WAVES * 64)
-    sm.wrow[m] = (STAGE == 1 && m < J.cnt) ? A.topk_w[A.perm[J.start + m]] : 0.0f;
+  // Tile row m: folded router weight and A row (gate/up: token perm / k of
+  // x's codes; down: plan row start + m of h's).  Rows past the tile's end
+  // read the tile's first row (never stored).
+  for (int m = tid; m < ROWS; m += WAVES * 64) {
+    const int mm = m < J.cnt ? m : 0;
+    if (STAGE == 1) {
+      const int f = A.perm[J.start + mm];
+      sm.wrow[m] = m < J.cnt ? A.topk_w[f] : 0.0f;
+      sm.src[m] = f / A.k;
+    } else {
+      sm.wrow[m] = 0.0f;
+      sm.src[m] = J.start + mm;
+    }
+  }
   __syncthreads();
 
-  // A rows are plan rows start .. start + cnt - 1 of the chunk-major layout
-  // (x's codes for gate/up, h's for down).  Rows past the tile's end read
-  // the tile's first row (never stored).
-  const size_t n = (size_t)A.T * A.k;
-  const size_t qstep = n * 64, sstep = n * 8;  // one chunk of codes, one chunk pair of scales
-  const uint8_t* qbase = (STAGE == 1 ? A.xq : A.hq) + (size_t)J.start * 64;
-  const uint8_t* sbase = (STAGE == 1 ? A.xsc : A.hsc) + (size_t)J.start * 8;
+  // chunk-major rows: one chunk of codes, one chunk pair of scales apart
+  const size_t n = STAGE == 1 ? (size_t)A.T : (size_t)A.T * A.k;
+  const size_t qstep = n * 64, sstep = n * 8;
+  const uint8_t* qbase = STAGE == 1 ? A.xq : A.hq;
+  const uint8_t* sbase = STAGE == 1 ? A.xsc : A.hsc;
   const uint8_t* aq[PPT];
   int aq_lds[PPT];
 #pragma unroll
   for (int j = 0; j < PPT; j++) {
     const int q = (tid + WAVES * 64 * j) % PIECES;  // piece q: row q / 4, K block q % 4
     const int r = q >> 2, kb = q & 3;
-    aq[j] = qbase + (r < J.cnt ? r : 0) * 64 + kb * 16;
+    aq[j] = qbase + (size_t)sm.src[r] * 64 + kb * 16;
     aq_lds[j] = mx_lds_index(r, kb);
   }
   // scales: thread tid stages row tid % ROWS (4 bytes a chunk)
   const int srow = tid % ROWS;
-  const uint8_t* as = sbase + (srow < J.cnt ? srow : 0) * 8;
+  const uint8_t* as = sbase + (size_t)sm.src[srow] * 8;
   const int s_lds = (srow & 15) * 8 + (srow >> 4);  // + kb * 128
 
   f32x4_t acc[NMF][4];
@@ -414,10 +421,9 @@ static hipError_t launch_mx_stages(const FfnArgs& a0, hipStream_t s) {
   const int slots = (a.routed_slots + a.shared_slots + 7) / 8 * 8;
   const int nb1 = col_blocks(max(a.F, a.n_shared ? a.Fs : 0) / H_COLS_WAVE);
   const int nb2 = col_blocks(a.d / OUT_COLS_WAVE);
-  const int n = a.T * a.k;
-  const int64_t blocks = (int64_t)n * (a.d / 32);
+  const int64_t blocks = (int64_t)a.T * (a.d / 32);
   x_to_mx_kernel<<<(unsigned)((blocks + 255) / 256), 256, 0, s>>>(
-      n, a.k, a.d, (const uint16_t*)a.hidden, a.perm, a.xq, a.xsc);
+      a.T, a.d, (const uint16_t*)a.hidden, a.xq, a.xsc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ffn_mx_kernel<SF, 1, MAXMF, LEAD_MX><<<slots * nb1, WAVES * 64, 0, s>>>(a);
