@@ -101,7 +101,7 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
   } while (0)
 
 // int4 / b-bit layers get the fp16 copy of x (and its per-token scales) from
-// the route plan's first launch.
+// the route plan's launches.
 bool x16_layer(const moe_desc* D) { return D->act == MOE_BF16 && ig32_bits(D->expert_w) != 0; }
 
 moe_status device_result(hipError_t e, const char* what) {

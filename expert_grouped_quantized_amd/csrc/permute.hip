@@ -14,8 +14,9 @@
 //                  (lanes holding the same expert id) plus per-wave counts in
 //                  LDS; perm/inv_perm scattered; chunk 0 also writes offsets
 //                  and the row-tile plan for the grouped GEMMs.
-// For int4 / b-bit layers the first launch also carries blocks that write the
-// fp16 copy of x the grouped gate/up products run on (see x16_blocks).
+// For int4 / b-bit layers the plan_scatter launch also carries blocks that
+// write the fp16 copy of x the grouped gate/up products run on (see
+// x16_blocks).
 // Only the histogram uses atomics, and counts do not depend on their order;
 // every position is a function of the input alone.
 #include "plan_kernels.h"
@@ -24,26 +25,19 @@ namespace moe {
 
 // Blocks past the plan's own that write the fp16 copy of an int4 (or b-bit)
 // layer's activations and its per-token scales (x given): one wave per token.
-// They share the plan's first launch (they need nothing from it), so the copy
-// costs no launch of its own and runs beside the histogram.
+// They share the plan_scatter launch (they need nothing from the plan), so
+// the copy costs no launch of its own and runs beside the plan's few blocks
+// (T=4096: 256 blocks beside 40; permute 22.0 -> 20.1 us against carrying
+// them in plan_count, whose histogram blocks finish first).
 constexpr int X16_TOKENS_PER_BLOCK = PLAN_THREADS / 64;
 inline int x16_blocks(int T, const uint16_t* x) {
   return x ? (T + X16_TOKENS_PER_BLOCK - 1) / X16_TOKENS_PER_BLOCK : 0;
 }
 
-// Blocks 0 .. n_chunks-1: one chunk's histogram each; blocks past them: the
-// fp16 copy of x (x given).
+// One chunk's histogram per block.
 __global__ __launch_bounds__(PLAN_THREADS) void plan_count_kernel(
-    int n, int E, int n_chunks, const int32_t* __restrict__ ids, int32_t* __restrict__ counts,
-    int T, int d, const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
-    float* __restrict__ xscale) {
+    int n, int E, const int32_t* __restrict__ ids, int32_t* __restrict__ counts) {
   __shared__ int hist[MAX_EXPERTS];
-  if ((int)blockIdx.x >= n_chunks) {
-    rows_to_f16(T, d, x, x16, xscale,
-                ((int)blockIdx.x - n_chunks) * X16_TOKENS_PER_BLOCK + (threadIdx.x >> 6),
-                ((int)gridDim.x - n_chunks) * X16_TOKENS_PER_BLOCK);
-    return;
-  }
   const int tid = threadIdx.x, base = blockIdx.x * PLAN_CHUNK;
   const int len = min(PLAN_CHUNK, n - base);
   for (int e = tid; e < E; e += PLAN_THREADS) hist[e] = 0;
@@ -81,8 +75,8 @@ hipError_t launch_tiles_from_offsets(int E, int rows, int slots, const int32_t* 
   return hipGetLastError();
 }
 
-// One chunk per block.  A one-chunk plan (the only launch of its plan) may
-// carry the blocks that write the fp16 copy of x (x given; see x16_blocks).
+// One chunk per block; blocks past the chunks write the fp16 copy of x (x
+// given; see x16_blocks).
 template <bool SINGLE>
 __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     int n, int E, int n_chunks, const int32_t* __restrict__ ids,
@@ -90,10 +84,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_scatter_kernel(
     int32_t* __restrict__ inv_perm, int rows, int slots, int4* __restrict__ tiles, int T, int d,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ x16, float* __restrict__ xscale) {
   __shared__ PlanSmem sm;
-  if (SINGLE && blockIdx.x > 0) {
+  const int nplan = SINGLE ? 1 : n_chunks;
+  if ((int)blockIdx.x >= nplan) {
     rows_to_f16(T, d, x, x16, xscale,
-                (blockIdx.x - 1) * X16_TOKENS_PER_BLOCK + (threadIdx.x >> 6),
-                (gridDim.x - 1) * X16_TOKENS_PER_BLOCK);
+                ((int)blockIdx.x - nplan) * X16_TOKENS_PER_BLOCK + (threadIdx.x >> 6),
+                ((int)gridDim.x - nplan) * X16_TOKENS_PER_BLOCK);
     return;
   }
   plan_scatter_block<SINGLE>(n, E, n_chunks, blockIdx.x, ids, counts, offsets, perm, inv_perm,
@@ -114,13 +109,12 @@ hipError_t launch_plan(int T, int k, int E, int rows, const int32_t* ids, int32_
         n, E, 1, ids, counts, offsets, perm, inv_perm, rows, L.routed_slots, tiles, T, d,
         x_for_f16, x16, xscale);
   } else {
-    plan_count_kernel<<<L.n_chunks + x16_blocks(T, x_for_f16), PLAN_THREADS, 0, s>>>(
-        n, E, L.n_chunks, ids, counts, T, d, x_for_f16, x16, xscale);
+    plan_count_kernel<<<L.n_chunks, PLAN_THREADS, 0, s>>>(n, E, ids, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    plan_scatter_kernel<false><<<L.n_chunks, PLAN_THREADS, 0, s>>>(
-        n, E, L.n_chunks, ids, counts, offsets, perm, inv_perm, rows, L.routed_slots, tiles, 0, 0,
-        nullptr, nullptr, nullptr);
+    plan_scatter_kernel<false><<<L.n_chunks + x16_blocks(T, x_for_f16), PLAN_THREADS, 0, s>>>(
+        n, E, L.n_chunks, ids, counts, offsets, perm, inv_perm, rows, L.routed_slots, tiles, T, d,
+        x_for_f16, x16, xscale);
   }
   return hipGetLastError();
 }
