@@ -69,10 +69,17 @@ __device__ __forceinline__ void router_small_block(int T, int d, int E, const ui
     const int e = e0 + (lane & 15);
     if (e < E) {
       const float bv = bias ? bias[e] : 0.0f;
+      const int tq = t0 + wave * 16 + 4 * (lane >> 4);  // this lane's 4 token rows
+      auto put = [&](int r) { logits[(size_t)(tq + r) * E + e] = s[r] + bv; };
+      // all four rows in range: four stores behind one branch (a branch per
+      // store makes each wait for the previous store to complete)
+      if (tq + 3 < T) {
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int t = t0 + wave * 16 + 4 * (lane >> 4) + r;
-        if (t < T) logits[(size_t)t * E + e] = s[r] + bv;
+        for (int r = 0; r < 4; r++) put(r);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (tq + r < T) put(r);
       }
     }
   }
