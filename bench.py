@@ -1,7 +1,8 @@
 """Benchmark of the MoE layer on one MI355X.
 
 A step is one pass of the whole layer -- moe_route -> moe_permute ->
-moe_grouped_ffn -> moe_combine -- over one batch of seeded synthetic input,
+moe_grouped_ffn -> moe_combine, with route and permute as one moe_route_plan
+call (a single launch) at T <= 32 -- over one batch of seeded synthetic input,
 inputs already resident in HBM.  The headline workload is the T=4096 prefill
 (int4 group-32 routed experts, int8 per-row shared expert, bf16 activations,
 d=2560, E=512, top-10 + 1 shared, expert width 1024); the T=16 decode/verify
@@ -84,10 +85,14 @@ class Setup:
         L.routed_blob = self.routed[i % N_ROT]
         if ev is not None:
             ev[0].record()
-        L.route(self.x, self.T)
+        if self.T <= 32:  # the layer's small-call front end: one launch
+            L.route_plan(self.x, self.T)
+        else:
+            L.route(self.x, self.T)
         if ev is not None:
             ev[1].record()
-        L.permute(self.x, self.T)
+        if self.T > 32:
+            L.permute(self.x, self.T)
         if ev is not None:
             ev[2].record()
         L.grouped_ffn(self.x, self.T)
@@ -118,8 +123,16 @@ def time_steps(S: Setup, steps: int, warmup: int):
     return wall, layer_ms, per_call
 
 
+def call_ms(per, T):
+    """Per-call HIP-event times of one step (route and permute are one
+    moe_route_plan call at T <= 32)."""
+    if T <= 32:
+        return dict(route_plan=per[0] + per[1], grouped_ffn=per[2], combine=per[3])
+    return dict(route=per[0], permute=per[1], grouped_ffn=per[2], combine=per[3])
+
+
 def time_graph(S: Setup, steps: int):
-    """The four calls captured as one HIP graph per routed-blob copy, replayed
+    """The layer's calls captured as one HIP graph per routed-blob copy, replayed
     back to back; wall clock and HIP-event time per replay."""
     torch = S.torch
     graphs = []
@@ -281,8 +294,7 @@ def run_prefill(args, torch, W):
     layer_tflops = (A["ffn_flops"] + A["router_flops"]) / (ms_per_step * 1e-3) / 1e12
     res = dict(T=cfg.T, tokens_per_s=cfg.T / (ms_per_step * 1e-3), ms_per_step=ms_per_step,
                layer_event_ms=layer_ms,
-               call_ms=dict(route=per_call[0], permute=per_call[1], grouped_ffn=per_call[2],
-                            combine=per_call[3]),
+               call_ms=call_ms(per_call, cfg.T),
                layer_tflops=layer_tflops, layer_mfma_frac=layer_tflops / BF16_PEAK_TFLOPS,
                layer_gbs=A["layer_bytes"] / (ms_per_step * 1e-3) / 1e9)
     roof = {"bound": "mfma", "kernel": "moe_grouped_ffn (gate/up + down GEMMs)",
@@ -306,7 +318,7 @@ def run_decode(args, torch, W):
     ffn_gbs = DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9
     res = dict(T=16, tokens_per_s=16 / (d_ms * 1e-3), ms_per_step=d_ms, active_experts=d_active,
                layer_event_ms=dlayer_ms,
-               call_ms=dict(route=dper[0], permute=dper[1], grouped_ffn=dper[2], combine=dper[3]),
+               call_ms=call_ms(dper, 16),
                weight_bytes=DA["weight_bytes"],
                layer_hbm_frac=DA["layer_bytes"] / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                ffn_weight_gbs=ffn_gbs)
@@ -395,7 +407,7 @@ def run_mxfp4(args, torch, W):
     A = algorithmic(cfg, cfg.T, act)
     ffn_s = per[2] * 1e-3
     pre = dict(T=cfg.T, tokens_per_s=cfg.T / (ms * 1e-3), ms_per_step=ms, layer_event_ms=layer_ms,
-               call_ms=dict(route=per[0], permute=per[1], grouped_ffn=per[2], combine=per[3]),
+               call_ms=call_ms(per, cfg.T),
                active_experts=act,
                ffn_tflops=A["ffn_flops"] / ffn_s / 1e12,
                ffn_fp4_mfma_frac=A["ffn_flops"] / ffn_s / 1e12 / FP4_PEAK_TFLOPS,
@@ -420,8 +432,7 @@ def run_mxfp4(args, torch, W):
             dwall, dlayer, dper = time_steps(D, args.decode_steps, 10)
             d_ms = dwall * 1e3 / args.decode_steps
             rec.update(tokens_per_s=T / (d_ms * 1e-3), ms_per_step=d_ms, layer_event_ms=dlayer,
-                       call_ms=dict(route=dper[0], permute=dper[1], grouped_ffn=dper[2],
-                                    combine=dper[3]),
+                       call_ms=call_ms(dper, T),
                        ffn_weight_gbs=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9,
                        ffn_weight_hbm_frac=DA["weight_bytes"] / (dper[2] * 1e-3) / 1e9 / HBM_PEAK_GBS)
             out["decode_roofline"] = {
@@ -470,7 +481,7 @@ def run_configs(args, torch, W, with_cpu=False):
         ffn_s = per[2] * 1e-3
         rec = dict(T=cfg.T, routed_w=cfg.expert, shared_w=cfg.shared, bound=bound,
                    tokens_per_s=cfg.T / (ms * 1e-3), ms_per_step=ms, layer_event_ms=layer_ms,
-                   call_ms=dict(route=per[0], permute=per[1], grouped_ffn=per[2], combine=per[3]),
+                   call_ms=call_ms(per, cfg.T),
                    active_experts=act, max_over_mean_load=float(counts.max() / counts.mean()),
                    ffn_tflops=A["ffn_flops"] / ffn_s / 1e12,
                    ffn_mfma_frac=A["ffn_flops"] / ffn_s / 1e12 / BF16_PEAK_TFLOPS,

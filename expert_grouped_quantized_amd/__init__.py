@@ -78,6 +78,8 @@ def lib():
             "moe_route": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
             "moe_route_from_logits": ([D, i32, i32, vp, vp, vp, vp], i32),
             "moe_permute": ([D, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+            "moe_route_plan": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+                               i32),
             "moe_grouped_ffn": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
             "moe_grouped_ffn_noalloc": ([D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "moe_combine": ([D, i32, i32, vp, vp, vp, vp, vp], i32),
@@ -180,6 +182,15 @@ def moe_permute(desc, T, k, hidden, topk_ids, offsets, perm, inv_perm, workspace
                              _p(perm), _p(inv_perm), _p(workspace),
                              _ws_bytes(workspace, workspace_bytes), _stream(stream)),
            "moe_permute")
+
+
+def moe_route_plan(desc, T, k, hidden, router_w, bias, logits, topk_ids, topk_w, offsets, perm,
+                   inv_perm, workspace, workspace_bytes=None, stream=None):
+    _check(lib().moe_route_plan(ctypes.byref(desc), T, k, _p(hidden), _p(router_w), _p(bias),
+                                _p(logits), _p(topk_ids), _p(topk_w), _p(offsets), _p(perm),
+                                _p(inv_perm), _p(workspace),
+                                _ws_bytes(workspace, workspace_bytes), _stream(stream)),
+           "moe_route_plan")
 
 
 def moe_grouped_ffn(desc, T, k, hidden, topk_w, offsets, perm, routed_blob, shared_blob,

@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "ffn.hip", "ffn_lowbit.hip", "ffn_mx.hip", "combine.hip",
+SOURCES = ["route.hip", "permute.hip", "route_plan.hip", "ffn.hip", "ffn_lowbit.hip", "ffn_mx.hip", "combine.hip",
            "noalloc.hip", "abi.cpp"]
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # keep the compiler from emitting packed-fp32 VALU instructions

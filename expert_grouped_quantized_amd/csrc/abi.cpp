@@ -677,6 +677,38 @@ moe_status moe_permute(const moe_desc* D, int32_t T, int32_t k, const void* hidd
                        "route-plan launch");
 }
 
+moe_status moe_route_plan(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
+                          const void* router_w, const float* bias, float* logits,
+                          int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* perm,
+                          int32_t* inv_perm, void* workspace, size_t ws_bytes, void* stream) {
+  TRY(check_desc(D));
+  TRY(check_tk(D, T, k));
+  TRY(check_ptr(hidden, "hidden"));
+  TRY(check_ptr(router_w, "router_w"));
+  if (bias) TRY(check_ptr(bias, "bias", 4));
+  TRY(check_ptr(logits, "logits"));
+  TRY(check_ptr(topk_ids, "topk_ids"));
+  TRY(check_ptr(topk_w, "topk_w"));
+  TRY(check_ptr(offsets, "offsets"));
+  TRY(check_ptr(perm, "perm"));
+  TRY(check_ptr(inv_perm, "inv_perm"));
+  TRY(check_ptr(workspace, "workspace", 256));
+  const WsLayout L = ws_layout(*D, T, k);
+  if (ws_bytes < L.total)
+    return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if (T == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  if (D->act == MOE_BF16 && T <= 32)
+    return device_result(
+        launch_route_plan_small(T, D->d, D->n_experts, k, hidden, router_w, bias, logits,
+                                topk_ids, topk_w, offsets, perm, inv_perm, tile_rows(T),
+                                workspace, L, x16_layer(D), s),
+        "route-plan launch");
+  TRY(moe_route(D, T, k, hidden, router_w, bias, logits, topk_ids, topk_w, stream));
+  return moe_permute(D, T, k, hidden, topk_ids, offsets, perm, inv_perm, workspace, ws_bytes,
+                     stream);
+}
+
 moe_status moe_grouped_ffn(const moe_desc* D, int32_t T, int32_t k, const void* hidden,
                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
                            const void* routed_blob, const void* shared_blob, float* out_assign,

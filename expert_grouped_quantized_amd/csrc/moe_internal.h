@@ -102,6 +102,9 @@ __host__ __device__ inline size_t expert_bytes(int fmt, size_t d, size_t F) {
 // Workspace layout, shared by moe_workspace_bytes, moe_permute and
 // moe_grouped_ffn.  Every region starts on a 256-byte boundary.
 struct WsLayout {
+  size_t ticket;       // int32 [4] at offset 0 for every T: the block counters
+                       //                       of moe_route_plan's one-launch form, zero
+                       //                       between calls (no other call writes them)
   int n_chunks;        // plan blocks
   int routed_slots;    // upper bound on routed row tiles
   size_t counts;       // int32 [n_chunks][E]   per-chunk expert histogram
@@ -130,6 +133,7 @@ inline WsLayout ws_layout(const moe_desc& D, int64_t T, int64_t k) {
   L.routed_slots = (int)(bound < n ? bound : n);
   size_t elem = D.act == MOE_F32 ? 4 : 2;
   size_t off = 0;
+  L.ticket = off;   off = align256(off + 16);
   L.counts = off;   off = align256(off + (size_t)L.n_chunks * D.n_experts * 4);
   L.tiles = off;    off = align256(off + (size_t)L.routed_slots * 16);
   const bool mx = D.act == MOE_BF16 && D.expert_w == MOE_MXFP4;
@@ -156,6 +160,13 @@ hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* ids, f
 hipError_t launch_plan(int T, int k, int E, int rows, const int32_t* ids, int32_t* offsets,
                        int32_t* perm, int32_t* inv_perm, void* ws, const WsLayout& L, int d,
                        const uint16_t* x_for_f16, hipStream_t s);
+// Router, top-k, plan and (with_x16) the fp16 copy of x in one launch, for
+// bf16 calls of at most 32 tokens (route_plan.hip); the workspace's counters
+// must be zero, and are zero again when the launch ends.
+hipError_t launch_route_plan_small(int T, int d, int E, int k, const void* x, const void* wr,
+                                   const float* bias, float* logits, int32_t* ids, float* w,
+                                   int32_t* offsets, int32_t* perm, int32_t* inv_perm, int rows,
+                                   void* ws, const WsLayout& L, bool with_x16, hipStream_t s);
 
 
 struct FfnArgs {

@@ -118,11 +118,16 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 // One wave per token; 4 tokens per 256-thread block.  Expert e lives in lane
 // e % 64, slot e / 64 (coalesced loads); PL slots a lane (8 for E <= 512, 16
-// for E <= 1024).  Each lane keeps its best remaining candidate (largest key,
-// lowest slot among equal keys).  Each of the k rounds takes a wave max of
-// those keys and -- only when several lanes hold that key -- a wave min of
-// their expert ids, so equal logits go to the lower id; only the winning lane
-// then rescans its slots.
+// for E <= 1024).  Candidates are ordered by (key descending, expert id
+// ascending); within a lane a lower slot is a lower id.  Each lane keeps its
+// best and second-best remaining candidates.  Each of the k rounds takes a
+// wave max of the lanes' best keys and -- only when several lanes hold that
+// key -- a wave min of their expert ids, so equal logits go to the lower id.
+// The winning lane marks the slot taken and promotes its second-best; a lane
+// that wins again before its next scan rescans its slots (past the taken
+// ones).  Per round that is a wave max, a ballot and a few moves in one lane,
+// instead of a scan of every slot of the winner.
+
 // Token t's logits, PL a lane (expert j * 64 + lane in slot j).  The loads
 // carry no condition (slots past E re-read the row's last logit), so they
 // issue back to back under one wait; a per-slot guarded load would wait for
@@ -137,27 +142,39 @@ __device__ __forceinline__ void topk_load(int t, int E, const float* __restrict_
 }
 
 // Top-k and softmax of token t from its loaded logits; writes ids / w (and,
-// if ids_lds is given, the ids at ids_lds[t * k + s] too).
+// if ids_lds is given, the ids at ids_lds[lds_row * k + s] too).
 template <int PL>
 __device__ __forceinline__ void topk_select(int t, int E, int k, const float (&lv)[PL],
                                             int32_t* __restrict__ ids, float* __restrict__ w,
-                                            int32_t* ids_lds = nullptr) {
+                                            int32_t* ids_lds = nullptr, int lds_row = 0) {
+  static_assert(PL <= 32, "the taken-slot mask is one dword");
   const int lane = threadIdx.x & 63;
   uint32_t key[PL];
 #pragma unroll
   for (int j = 0; j < PL; j++) key[j] = j * 64 + lane < E ? order_key(lv[j]) : 0u;
   auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
   auto umin = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
-  uint32_t bk = 0;
-  int bj = 0;
-  auto lane_best = [&]() {
-    bk = 0;
-    bj = 0;
+  // the lane's best (bk, bj) and second-best (nk, nj) untaken candidates; a
+  // strict > over ascending slots keeps the lower slot first among equal keys
+  // (selects, no branches: every lane runs the same instructions)
+  uint32_t bk = 0, nk = 0, taken = 0;
+  int bj = 0, nj = 0;
+  auto lane_top2 = [&]() __attribute__((always_inline)) {
+    uint32_t k1 = 0, k2 = 0;
+    int j1 = 0, j2 = 0;
 #pragma unroll
-    for (int j = 0; j < PL; j++)
-      if (key[j] > bk) { bk = key[j]; bj = j; }
+    for (int j = 0; j < PL; j++) {
+      const uint32_t kj = (taken >> j) & 1u ? 0u : key[j];
+      const bool gt1 = kj > k1, gt2 = kj > k2;
+      k2 = gt1 ? k1 : gt2 ? kj : k2;
+      j2 = gt1 ? j1 : gt2 ? j : j2;
+      k1 = gt1 ? kj : k1;
+      j1 = gt1 ? j : j1;
+    }
+    bk = k1; bj = j1; nk = k2; nj = j2;
   };
-  lane_best();
+  lane_top2();
+  bool have2 = true;  // (nk, nj) is the true second-best since the last scan
   int my_id = 0;
   float my_logit = 0.0f, top_logit = 0.0f;
   for (int s = 0; s < k; s++) {
@@ -169,11 +186,16 @@ __device__ __forceinline__ void topk_select(int t, int E, int k, const float (&l
       e = (uint32_t)__builtin_amdgcn_readlane((int)my_e, __ffsll((long long)holders) - 1);
     else
       e = wave_reduce_u32(bk == m ? my_e : 0xFFFFFFFFu, umin);
-    if (my_e == e) {  // the winning lane drops the candidate and rescans
-#pragma unroll
-      for (int j = 0; j < PL; j++)
-        if (j == bj) key[j] = 0u;
-      lane_best();
+    if (my_e == e) {  // the winning lane
+      taken |= 1u << bj;
+      if (have2) {  // its second-best (0: none left) moves up
+        bk = nk;
+        bj = nj;
+        have2 = false;
+      } else {  // it won twice since its last scan: rescan past the taken slots
+        lane_top2();
+        have2 = true;
+      }
     }
     const float lg = key_to_float(m);
     if (s == 0) top_logit = lg;
@@ -184,7 +206,7 @@ __device__ __forceinline__ void topk_select(int t, int E, int k, const float (&l
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     w[(size_t)t * k + lane] = ex / sum;
-    if (ids_lds) ids_lds[t * k + lane] = my_id;
+    if (ids_lds) ids_lds[lds_row * k + lane] = my_id;
   }
 }
 

@@ -1,12 +1,14 @@
-"""MoELayer: holds the device buffers of one layer and issues the four C-ABI
-calls in order (route -> permute -> grouped_ffn -> combine).  Torch provides
-the device memory and the stream; nothing here computes."""
+"""MoELayer: holds the device buffers of one layer and issues the C-ABI calls
+in order (route + permute as one moe_route_plan call -> grouped_ffn ->
+combine).  Torch provides the device memory and the stream; nothing here
+computes."""
 from __future__ import annotations
 
 import numpy as np
 
 from . import (MOE_BLOB_ROUTED, MOE_BLOB_SHARED, MOE_F32, moe_blob_bytes, moe_combine,
-               moe_grouped_ffn, moe_pack_experts, moe_permute, moe_route, moe_workspace_bytes)
+               moe_grouped_ffn, moe_pack_experts, moe_permute, moe_route, moe_route_plan,
+               moe_workspace_bytes)
 
 
 def pack_blob(desc, kind, gate, gate_s, up, up_s, down, down_s) -> np.ndarray:
@@ -37,7 +39,8 @@ class MoELayer:
         self.shared_out = z((max(T_max, 1), d), f32) if desc.n_shared else None
         self.y = z((max(T_max, 1), d), act)
         self.ws_bytes = moe_workspace_bytes(desc, T_max, k)
-        self.workspace = z((self.ws_bytes,), torch.uint8)
+        # zeroed once: its first 16 bytes are moe_route_plan's block counters
+        self.workspace = torch.zeros((self.ws_bytes,), dtype=torch.uint8, device=device)
         self.router_w = self.bias = self.routed_blob = self.shared_blob = None
 
     def set_weights(self, router_w, routed_blob, shared_blob=None, bias=None):
@@ -53,6 +56,12 @@ class MoELayer:
         moe_permute(self.desc, T, self.k, x, self.ids, self.offsets, self.perm, self.inv_perm,
                     self.workspace, self.ws_bytes)
 
+    def route_plan(self, x, T):
+        """route and permute as one call (one launch when T <= 32, bf16)."""
+        moe_route_plan(self.desc, T, self.k, x, self.router_w, self.bias, self.logits, self.ids,
+                       self.w, self.offsets, self.perm, self.inv_perm, self.workspace,
+                       self.ws_bytes)
+
     def grouped_ffn(self, x, T):
         moe_grouped_ffn(self.desc, T, self.k, x, self.w, self.offsets, self.perm,
                         self.routed_blob, self.shared_blob, self.out_assign, self.shared_out,
@@ -65,14 +74,13 @@ class MoELayer:
         """x: device tensor [T, d] (act dtype).  Returns a view of y [T, d]."""
         T = x.shape[0] if T is None else T
         assert T <= self.T_max
-        self.route(x, T)
-        self.permute(x, T)
+        self.route_plan(x, T)
         self.grouped_ffn(x, T)
         self.combine(T)
         return self.y[:T]
 
     def capture(self, x, T=None):
-        """Record the four calls on x (a static device buffer) into one HIP
+        """Record the layer's calls on x (a static device buffer) into one HIP
         graph; replaying it reruns the layer on whatever x then holds, with the
         weights bound at capture time.  Returns the torch graph object."""
         import torch

@@ -141,11 +141,16 @@ const char* moe_status_str(int32_t status);
 const char* moe_last_error(void);
 
 /* Bytes of the device blob that holds the routed experts (kind ROUTED) or the
- * shared expert (kind SHARED) of `desc`.  Host only, no GPU touched.        */
+ * shared expert (kind SHARED) of `desc`: the expert packs of the
+ * "Qwen3.8-Flash-Next-Dual-GPU" README, "Model artifact and memory
+ * placement" table (routed experts as grouped int4/int8 codes beside their
+ * scales, resident on the GPU).  Host only, no GPU touched.                 */
 moe_status moe_blob_bytes(const moe_desc* desc, int32_t kind, size_t* bytes);
 
 /* Pack canonical weights (layouts above; `*_scales` NULL for F32/BF16) into
- * the private device blob, written to the host buffer `blob` of `blob_bytes`
+ * the private device blob (the expert packs of the same README table; the
+ * b-bit codes of the TandemLLM roadmap's "A mixture-of-experts model, and
+ * what is left"), written to the host buffer `blob` of `blob_bytes`
  * (>= moe_blob_bytes).  The caller copies it to device memory.  For ROUTED the
  * inputs hold n_experts experts stacked; for SHARED one expert.
  * MOE_I4_G32 codes must lie in [-7, 7] (symmetric); an 8 (-8) code returns
@@ -168,8 +173,11 @@ moe_status moe_unpack_experts(const moe_desc* desc, int32_t kind, const void* bl
                               size_t blob_bytes, void* gate, void* gate_scales, void* up,
                               void* up_scales, void* down, void* down_scales);
 
-/* Bytes of device workspace that moe_permute and moe_grouped_ffn need for T
- * tokens and top-k.  Nothing in it needs initializing.  Host only.         */
+/* Bytes of device workspace that moe_permute, moe_route_plan and
+ * moe_grouped_ffn need for T tokens and top-k (the route plan and the
+ * intermediate h of the README's "Dedicated prefill lane", steps 1-3).  Nothing in it needs
+ * initializing, except the first 16 bytes for moe_route_plan (zero; see
+ * there).  Host only.                                                      */
 moe_status moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t k, size_t* bytes);
 
 /* ------------------------------------------------------------------ device */
@@ -213,6 +221,27 @@ moe_status moe_permute(const moe_desc* desc, int32_t T, int32_t k, const void* h
                        const int32_t* topk_ids, int32_t* offsets, int32_t* perm,
                        int32_t* inv_perm, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* moe_route followed by moe_permute, as one call: the same arguments, the
+ * same outputs bit for bit (logits, topk_ids, topk_w, offsets, perm,
+ * inv_perm, and in the workspace the row-tile plan and the fp16 copy of
+ * hidden that moe_grouped_ffn reads).  For a small call -- act BF16 and
+ * T <= 32, where launches and latency rather than bytes set the time --
+ * it is a single kernel launch (TandemLLM Roadmap v0.11.2, "Parallel
+ * requests": a joint pass of up to 32 rows should cost about what its bytes
+ * cost); otherwise it issues moe_route's and moe_permute's launches.
+ *   workspace  >= moe_workspace_bytes(desc, T, k).  Its first 16 bytes
+ *              hold the single launch's block counters: they must be zero
+ *              before the first moe_route_plan call on this workspace (zero
+ *              them once after allocating it); every call leaves them zero,
+ *              and no other call writes them.  Calls that share a workspace
+ *              must be ordered (one stream), as for moe_permute.
+ * Errors as moe_route and moe_permute.                                    */
+moe_status moe_route_plan(const moe_desc* desc, int32_t T, int32_t k, const void* hidden,
+                          const void* router_w, const float* bias, float* logits,
+                          int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* perm,
+                          int32_t* inv_perm, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Expert-grouped SwiGLU ("Dedicated prefill lane", steps 2-4).  For each
  * expert e and each p in [offsets[e], offsets[e+1]), with f = perm[p],

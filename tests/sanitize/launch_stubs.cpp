@@ -23,6 +23,11 @@ hipError_t launch_plan(int, int, int, int, const int32_t*, int32_t*, int32_t*, i
                        const WsLayout&, int, const uint16_t*, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_route_plan_small(int, int, int, int, const void*, const void*, const float*,
+                                   float*, int32_t*, float*, int32_t*, int32_t*, int32_t*, int,
+                                   void*, const WsLayout&, bool, hipStream_t) {
+  return hipErrorNoDevice;
+}
 hipError_t launch_ffn_bf16(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_ffn_f32(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_ffn_lowbit(const FfnArgs&, hipStream_t) { return hipErrorNoDevice; }

@@ -116,6 +116,37 @@ def test_workspace_too_small():
 
 
 
+def _route_plan(desc, T=16, k=10, ws_bytes=None, **ptrs):
+    p = dict(hidden=FAKE, rw=FAKE, bias=None, logits=FAKE, ids=FAKE, w=FAKE, offsets=FAKE,
+             perm=FAKE, inv=FAKE, ws=FAKE)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = M.moe_workspace_bytes(desc, T, k)
+    return M.lib().moe_route_plan(ctypes.byref(desc), T, k, p["hidden"], p["rw"], p["bias"],
+                                  p["logits"], p["ids"], p["w"], p["offsets"], p["perm"],
+                                  p["inv"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("field", ["hidden", "rw", "logits", "ids", "w", "offsets", "perm", "inv"])
+def test_route_plan_pointer_checks(field):
+    assert _route_plan(_desc(), **{field: None}) == M.MOE_EINVAL
+    assert "NULL" in M.moe_last_error()
+    assert _route_plan(_desc(), **{field: FAKE + 4}) == M.MOE_EINVAL
+    assert "aligned" in M.moe_last_error()
+
+
+def test_route_plan_workspace_and_T_zero():
+    desc = _desc()
+    for T in (16, 32, 33, 4096):
+        need = M.moe_workspace_bytes(desc, T, 10)
+        assert _route_plan(desc, T=T, ws_bytes=need - 1) == M.MOE_EWORKSPACE
+        assert "workspace" in M.moe_last_error()
+        assert _route_plan(desc, T=T, ws=FAKE + 16) == M.MOE_EINVAL  # 256-byte alignment
+    assert _route_plan(desc, k=0, ws_bytes=1 << 30) == M.MOE_EINVAL
+    # no GPU here: any launch would fail, so OK proves nothing was enqueued
+    assert _route_plan(desc, T=0) == M.MOE_OK
+
+
 def test_shared_pointers_must_match_n_shared():
     desc = _desc(n_shared=0)
     ws = M.moe_workspace_bytes(desc, 8, 10)
