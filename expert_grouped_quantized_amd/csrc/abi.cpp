@@ -165,15 +165,21 @@ struct OutIO {  // canonical outputs of unpacking
 };
 
 // Position in lane l's stream of bit `k` of u = code + 2^(b-1), the offset
-// binary of element i (0..7) of fragment fi = 2 f + s.
-//   b = 2, 3 (bit planes, so the kernels cut out a pair of codes with one
-//   AND-OR): bits 0-1 in dword fi / 2 at 8 (fi % 2) + 16 (i % 2) + 2 (i / 2);
-//   b = 3's bit 2 in dword 4 + fi / 4 at 4 (fi % 4) + 16 (i % 2) + i / 2.
+// binary of element i (0..7) of fragment fi = 2 f + s.  Elements 2j and 2j+1
+// form pair j; an even element sits in a dword's low half, the odd one at the
+// same place in its high half, so the kernels cut a pair out with one AND-OR.
+//   b = 2: u in dword fi / 2 at 8 (fi % 2) + 16 (i % 2) + 2 (i / 2).
+//   b = 3: pair P = 4 fi + i / 2 of the lane's 32; P < 30: u in dword P / 5
+//   at 16 (i % 2) + 3 (P % 5) (five 3-bit fields a half); P = 30, 31: bit k
+//   of u at bit 15 + 16 (i % 2) of dword 3 (P - 30) + k (the halves' spare
+//   top bits).
 //   b = 5..8: one little-endian stream, element i at bit fi 8 b + i b.
 inline int ig32_bit_pos(int b, int fi, int i, int k) {
-  if (b == 2 || b == 3) {
-    if (k < 2) return 32 * (fi >> 1) + 8 * (fi & 1) + 16 * (i & 1) + 2 * (i >> 1) + k;
-    return 32 * (4 + (fi >> 2)) + 4 * (fi & 3) + 16 * (i & 1) + (i >> 1);
+  if (b == 2) return 32 * (fi >> 1) + 8 * (fi & 1) + 16 * (i & 1) + 2 * (i >> 1) + k;
+  if (b == 3) {
+    const int P = 4 * fi + (i >> 1), half = 16 * (i & 1);
+    if (P < 30) return 32 * (P / 5) + half + 3 * (P % 5) + k;
+    return 32 * (3 * (P - 30) + k) + half + 15;
   }
   return fi * 8 * b + i * b + k;
 }

@@ -279,21 +279,21 @@ struct WTileB {
     return r;
   }
 };
-// ---- 2- and 3-bit codes: bit planes laid out for pair extraction ---------
-// The low two bits of u = code + 2^(b-1) of element i (0..7) of fragment
-// fi = 2 f + s sit in stream dword fi / 2 at bit 8 (fi % 2) + 16 (i % 2) +
-// 2 (i / 2): the even elements in the low half, the odd ones in the high
-// half, so one AND-OR with 3 << 2j (in both halves) and the fp16 exponent of
-// 1024 gives the pair (2j, 2j+1) as two fp16 values 1024 + 4^j u2, exact.
-// For b = 3 the high bit of u sits in dword 4 + fi / 4 at bit 4 (fi % 4) +
-// 16 (i % 2) + i / 2 and reads as 1024 + 2^j u1 the same way.  Two (b = 2)
-// or three (b = 3) packed-fp16 ops per pair then make the codes exact, and
-// one packed multiply by the group scale rounds each product to nearest even
-// (fp16 MFMA); the bf16 form scales the exact codes in fp32 and rounds once
-// at the pack.  Group scales as in WTileB: [row c][f][s] at 512 b + c*16.
+// ---- 2- and 3-bit codes: laid out for pair extraction ---------------------
+// Elements 2j and 2j+1 of a fragment (pair j) sit at the same bits of a
+// dword's low and high halves, so one AND-OR with a field mask (in both
+// halves) and the fp16 exponent of 1024 gives the pair as two fp16 values
+// 1024 + 2^p u, exact, for u = code + 2^(b-1) at bit p <= 7 of its half.
+//   b = 2: u of pair j of fragment fi = 2 f + s in stream dword fi / 2 at
+//   bit 8 (fi % 2) + 2 j of each half.
+//   b = 3: pair P = 4 fi + j of the lane's 32; pairs 0-29 fill five 3-bit
+//   fields a half (u at bit 3 (P % 5) of dword P / 5; the fields at bits 9
+//   and 12 are read from the dword shifted right by 9), pairs 30 and 31 the
+//   halves' spare top bits: bit k of u at bit 15 of dword 3 (P - 30) + k.
+// Group scales as in WTileB: [row c][f][s] at 512 b + c*16.
 template <int B>
 struct WTileP {
-  static_assert(B == 2 || B == 3, "bit-plane tiles hold 2- or 3-bit codes");
+  static_assert(B == 2 || B == 3, "pair-extraction tiles hold 2- or 3-bit codes");
   static constexpr int NDW = 2 * B;
   uint32_t w[NDW];
   u32x4_t sc;
@@ -314,51 +314,62 @@ struct WTileP {
     const uint32_t sw = sc[si >> 1];
     return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
   }
-  // the 4 exact code pairs of fragment (f, s), as packed fp16
-  __device__ __forceinline__ void codes(int f, int s, f16x2_t (&c)[4]) const {
+  // pair j of fragment (f, s) as two fp16 values 1024 + 2^p u under the
+  // exponent of 1024 (p: the bit of u in its half, a constant once unrolled)
+  __device__ __forceinline__ uint32_t pair_bits(int f, int s, int j, int& p) const {
     const int fi = 2 * f + s;
-    const uint32_t q2 = (fi & 1) ? w[fi >> 1] >> 8 : w[fi >> 1];
-    uint32_t q1 = 0;
-    if constexpr (B == 3) q1 = w[4 + (fi >> 2)] >> (4 * (fi & 3));
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f16x2_t t2 =
-          __builtin_bit_cast(f16x2_t, and_or_b32(q2, 0x00030003u << (2 * j), 0x64006400u));
-      // 4^-j scales the low plane down to 1024 4^-j + u2
-      const _Float16 k2 = (_Float16)(1.0f / (float)(1 << (2 * j)));
-      if constexpr (B == 2) {
-        const _Float16 o = (_Float16)(-(1024.0f / (float)(1 << (2 * j)) + 2.0f));
-        c[j] = t2 * f16x2_t{k2, k2} + f16x2_t{o, o};
-      } else {
-        const f16x2_t t1 =
-            __builtin_bit_cast(f16x2_t, and_or_b32(q1, 0x00010001u << j, 0x64006400u));
-        // 4 u1 - 1024 4^-j - 4, exact: t1 (4 2^-j) = 4096 2^-j + 4 u1
-        const _Float16 k1 = (_Float16)(4.0f / (float)(1 << j));
-        const _Float16 o = (_Float16)(-(4096.0f / (float)(1 << j) + 1024.0f / (float)(1 << (2 * j)) +
-                                        4.0f));
-        c[j] = t2 * f16x2_t{k2, k2} + (t1 * f16x2_t{k1, k1} + f16x2_t{o, o});
+    constexpr uint32_t magic = 0x64006400u;
+    if constexpr (B == 2) {
+      const uint32_t q = (fi & 1) ? w[fi >> 1] >> 8 : w[fi >> 1];
+      p = 2 * j;
+      return and_or_b32(q, 0x00030003u << p, magic);
+    } else {
+      const int P = 4 * fi + j;
+      if (P < 30) {
+        const int fld = P % 5;
+        const uint32_t q = fld < 3 ? w[P / 5] : w[P / 5] >> 9;
+        p = 3 * (fld < 3 ? fld : fld - 3);
+        return and_or_b32(q, 0x00070007u << p, magic);
       }
+      const int d0 = 3 * (P - 30);
+      p = 0;
+      uint32_t t = and_or_b32(w[d0] >> 15, 0x00010001u, magic);
+      t = and_or_b32(w[d0 + 1] >> 14, 0x00020002u, t);
+      return and_or_b32(w[d0 + 2] >> 13, 0x00040004u, t);
     }
   }
+  // fp16(code * scale): (1024 + 2^p u) 2^-p - (1024 2^-p + 2^(b-1)) is the
+  // code, exact (one packed fma); one packed multiply by the scale rounds
+  // each product to nearest even
   __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
     const f16x2_t s2 = scale_splat(sc, f * 2 + s);
-    f16x2_t c[4];
-    codes(f, s, c);
     u32x4_t r;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const f16x2_t p = c[j] * s2;
-      r[j] = __builtin_bit_cast(uint32_t, p);
+      int p;
+      const uint32_t t = pair_bits(f, s, j, p);
+      const _Float16 k = (_Float16)(1.0f / (float)(1 << p));
+      const _Float16 o = (_Float16)(-(1024.0f / (float)(1 << p) + (float)(1 << (B - 1))));
+      const f16x2_t c = __builtin_bit_cast(f16x2_t, t) * f16x2_t{k, k} + f16x2_t{o, o};
+      r[j] = __builtin_bit_cast(uint32_t, c * s2);
     }
     return r;
   }
+  // bf16(code * scale): one mixed-precision fma per value takes the fp16
+  // 1024 + 2^p u with scale 2^-p and the bias -(1024 2^-p + 2^(b-1)) scale
+  // (every product exact in fp32, so the sum is code * scale exactly); the
+  // pack rounds to nearest even
   __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
     const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
-    f16x2_t c[4];
-    codes(f, s, c);
     u32x4_t r;
 #pragma unroll
-    for (int j = 0; j < 4; j++) r[j] = pack_bf16x2((float)c[j][0] * scale, (float)c[j][1] * scale);
+    for (int j = 0; j < 4; j++) {
+      int p;
+      const f16x2_t t = __builtin_bit_cast(f16x2_t, pair_bits(f, s, j, p));
+      const float sp = scale * (1.0f / (float)(1 << p));
+      const float b = scale * -(1024.0f / (float)(1 << p) + (float)(1 << (B - 1)));
+      r[j] = pack_bf16x2(fmaf((float)t[0], sp, b), fmaf((float)t[1], sp, b));
+    }
     return r;
   }
 };
