@@ -164,24 +164,22 @@ struct OutIO {  // canonical outputs of unpacking
   uint8_t* s;
 };
 
-// Position in lane l's stream of bit `k` of u = code + 2^(b-1), the offset
-// binary of element i (0..7) of fragment fi = 2 f + s.  Elements 2j and 2j+1
-// form pair j; an even element sits in a dword's low half, the odd one at the
-// same place in its high half, so the kernels cut a pair out with one AND-OR.
-//   b = 2: u in dword fi / 2 at 8 (fi % 2) + 16 (i % 2) + 2 (i / 2).
-//   b = 3: pair P = 4 fi + i / 2 of the lane's 32; P < 30: u in dword P / 5
-//   at 16 (i % 2) + 3 (P % 5) (five 3-bit fields a half); P = 30, 31: bit k
-//   of u at bit 15 + 16 (i % 2) of dword 3 (P - 30) + k (the halves' spare
-//   top bits).
-//   b = 5..8: one little-endian stream, element i at bit fi 8 b + i b.
+// Position in lane l's 2b dwords of bit `k` of u = code + 2^(b-1), the
+// offset binary of element i (0..7) of fragment fi = 2 f + s.  Elements 2j
+// and 2j+1 form pair P = 4 fi + j; the even element sits in a dword's low
+// half-word, the odd one at the same bits of its high half-word, so the
+// kernels cut a pair out with one AND-OR.  Each half-word holds NF = 16 / b
+// fields of b bits: pair P < 2 b NF at bit b (P % NF) of dword P / NF; the
+// remaining pairs take the half-words' SB = 16 - NF b spare top bits in turn,
+// bit k of the q-th such pair at spare bit g = q b + k, i.e. bit NF b + g % SB
+// of dword g / SB.  (b = 2: dword fi / 2 at 8 (fi % 2) + 2 j; b = 3: five
+// fields a half, pairs 30-31 in the spare bits.)
 inline int ig32_bit_pos(int b, int fi, int i, int k) {
-  if (b == 2) return 32 * (fi >> 1) + 8 * (fi & 1) + 16 * (i & 1) + 2 * (i >> 1) + k;
-  if (b == 3) {
-    const int P = 4 * fi + (i >> 1), half = 16 * (i & 1);
-    if (P < 30) return 32 * (P / 5) + half + 3 * (P % 5) + k;
-    return 32 * (3 * (P - 30) + k) + half + 15;
-  }
-  return fi * 8 * b + i * b + k;
+  const int nf = 16 / b, sb = 16 - nf * b, npf = 2 * b * nf;
+  const int P = 4 * fi + (i >> 1), half = 16 * (i & 1);
+  if (P < npf) return 32 * (P / nf) + half + b * (P % nf) + k;
+  const int g = (P - npf) * b + k;
+  return 32 * (g / sb) + half + nf * b + g % sb;
 }
 
 // b-bit group-32 tile: lane l's codes of fragment f, K step s, at the bit

@@ -203,19 +203,35 @@ struct WTile<MOE_I8_ROW> {
   }
 };
 
-// ---- b-bit group-32 codes (b = 5, 6, 7, 8) ------------------------------
-// Lane l's codes of a wave tile form one little-endian bit stream of 64 b
-// bits: code i (0..7) of fragment f, K step s at bit (2 f + s) 8 b + i b, as
-// code + 2^(b-1) (offset binary).  The stream's dwords sit in 16-byte groups
-// (group g of all lanes at g*1024 + lane*16), an odd b ending with one
-// 8-byte group (at G*1024 + lane*8); the fp16 group scales follow at 512 b,
-// as in the int4 tile.  So every load is a coalesced wave-wide run and the
-// blob holds exactly b bits per weight plus the scales.
+// ---- b-bit group-32 codes (b = 2, 3, 5, 6, 7, 8) -------------------------
+// Lane l's 64 codes of a wave tile, each as u = code + 2^(b-1) (offset
+// binary), fill 2b dwords: the dwords sit in 16-byte groups (group g of all
+// lanes at g*1024 + lane*16), an odd b ending with one 8-byte group (at
+// G*1024 + lane*8); the fp16 group scales follow at 512 b ([row c][f][s] at
+// 512 b + c*16), as in the int4 tile.  So every load is a coalesced wave-wide
+// run and the blob holds exactly b bits per weight plus the scales.
+// Elements 2j and 2j+1 of fragment fi = 2 f + s form pair P = 4 fi + j of the
+// lane's 32; the even element sits in a dword's low half-word and the odd one
+// at the same bits of its high half-word, so one AND-OR with a field mask (in
+// both halves) and the fp16 exponent of 1024 cuts a pair out as two fp16
+// values 1024 + 2^p u, exact (p + b <= 10).  Each half-word holds NF = 16 / b
+// fields of b bits: pair P < 2 b NF has u in dword P / NF at bit b (P % NF)
+// (a field that ends past bit 10 is read from the dword shifted down to bit
+// 0); the last 32 - 2 b NF pairs take the half-words' SB = 16 - NF b spare
+// top bits in turn: bit k of the q-th such pair's u is spare bit g = q b + k,
+// at bit NF b + g % SB of dword g / SB.  (b = 2: 8 fields a half; b = 3: 5
+// fields, pairs 30-31 in the spare bits; b = 8: 2 fields.)  ig32_bit_pos in
+// the packer is the same map.
 template <int B>
-struct WTileB {
-  static constexpr int NDW = 2 * B;    // stream dwords per lane
+struct WTileP {
+  static_assert(B >= 2 && B <= 8 && B != 4, "group-32 codes of 2, 3, 5, 6, 7 or 8 bits");
+  static constexpr int NDW = 2 * B;    // dwords per lane
   static constexpr int G = NDW / 4;    // full 16-byte groups
   static constexpr bool TAIL = NDW % 4 != 0;
+  static constexpr int NF = 16 / B;    // fields per half-word
+  static constexpr int SB = 16 - NF * B;  // spare top bits per half-word
+  static constexpr int NPF = 2 * B * NF;  // pairs held in fields
+  static_assert(NPF + (NDW * SB) / B == 32 && (NDW * SB) % B == 0, "every pair has its bits");
   uint32_t w[NDW];
   u32x4_t sc;
   template <bool NT>
@@ -238,105 +254,34 @@ struct WTileB {
     const uint32_t sw = sc[si >> 1];
     return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
   }
-  // bits [o, o + n) of the stream, n <= 16 (o, n constant once unrolled)
-  __device__ __forceinline__ uint32_t field(int o, int n) const {
-    const int d = o >> 5, sh = o & 31;
-    const uint32_t win = sh + n <= 32 ? w[d] >> sh : __builtin_amdgcn_alignbit(w[d + 1], w[d], sh);
-    return win & ((1u << n) - 1);
-  }
-  // fp16(code * scale): each pair of codes under the fp16 exponent of 1024
-  // reads as 1024 + code + 2^(b-1); one packed subtract makes the codes exact,
-  // one packed multiply by the scale rounds each product to nearest even.
-  __device__ __forceinline__ u32x4_t frag16(int f, int s, const F16Consts&) const {
-    // integer splat of the scale: the op_sel form (scale_splat) makes the
-    // 96-row 2- and 7-bit gate/up kernels spill
-    const uint32_t sb = scale_bits(f, s);
-    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sb | (sb << 16));
-    constexpr _Float16 bias = (_Float16)(-(1024 + (1 << (B - 1))));
-    const f16x2_t off = {bias, bias};
-    const int base = (2 * f + s) * 8 * B;
-    u32x4_t r;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint32_t lo = field(base + 2 * j * B, B), hi = field(base + (2 * j + 1) * B, B);
-      const uint32_t t = ((hi << 16) | lo) | 0x64006400u;
-      r[j] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, t) + off) * s2);
-    }
-    return r;
-  }
-  // bf16(code * scale): code + 2^(b-1) as a float, one FMA with the scale
-  // (exact in fp32), rounded to nearest even by the pack
-  __device__ __forceinline__ u32x4_t frag(int f, int s, const F16Consts&) const {
-    const float scale = f16_bits_to_f32((uint16_t)scale_bits(f, s));
-    const float bias = -(float)(1 << (B - 1)) * scale;
-    const int base = (2 * f + s) * 8 * B;
-    u32x4_t r;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const float a = (float)field(base + 2 * j * B, B), b = (float)field(base + (2 * j + 1) * B, B);
-      r[j] = pack_bf16x2(fmaf(a, scale, bias), fmaf(b, scale, bias));
-    }
-    return r;
-  }
-};
-// ---- 2- and 3-bit codes: laid out for pair extraction ---------------------
-// Elements 2j and 2j+1 of a fragment (pair j) sit at the same bits of a
-// dword's low and high halves, so one AND-OR with a field mask (in both
-// halves) and the fp16 exponent of 1024 gives the pair as two fp16 values
-// 1024 + 2^p u, exact, for u = code + 2^(b-1) at bit p <= 7 of its half.
-//   b = 2: u of pair j of fragment fi = 2 f + s in stream dword fi / 2 at
-//   bit 8 (fi % 2) + 2 j of each half.
-//   b = 3: pair P = 4 fi + j of the lane's 32; pairs 0-29 fill five 3-bit
-//   fields a half (u at bit 3 (P % 5) of dword P / 5; the fields at bits 9
-//   and 12 are read from the dword shifted right by 9), pairs 30 and 31 the
-//   halves' spare top bits: bit k of u at bit 15 of dword 3 (P - 30) + k.
-// Group scales as in WTileB: [row c][f][s] at 512 b + c*16.
-template <int B>
-struct WTileP {
-  static_assert(B == 2 || B == 3, "pair-extraction tiles hold 2- or 3-bit codes");
-  static constexpr int NDW = 2 * B;
-  uint32_t w[NDW];
-  u32x4_t sc;
-  template <bool NT>
-  __device__ __forceinline__ void load(const BufSrc& t, int lane) {
-    const u32x4_t v = t.ld16<NT>((uint32_t)(lane * 16));
-#pragma unroll
-    for (int c = 0; c < 4; c++) w[c] = v[c];
-    if constexpr (B == 3) {
-      const uint64_t h = t.ld8<NT>((uint32_t)(1024 + lane * 8));
-      w[4] = (uint32_t)h;
-      w[5] = (uint32_t)(h >> 32);
-    }
-    sc = t.ld16<NT>((uint32_t)(512 * B + (lane & 15) * 16));
-  }
-  __device__ __forceinline__ uint32_t scale_bits(int f, int s) const {
-    const int si = f * 2 + s;
-    const uint32_t sw = sc[si >> 1];
-    return (si & 1) ? (sw >> 16) : (sw & 0xffffu);
-  }
   // pair j of fragment (f, s) as two fp16 values 1024 + 2^p u under the
   // exponent of 1024 (p: the bit of u in its half, a constant once unrolled)
   __device__ __forceinline__ uint32_t pair_bits(int f, int s, int j, int& p) const {
-    const int fi = 2 * f + s;
     constexpr uint32_t magic = 0x64006400u;
-    if constexpr (B == 2) {
-      const uint32_t q = (fi & 1) ? w[fi >> 1] >> 8 : w[fi >> 1];
-      p = 2 * j;
-      return and_or_b32(q, 0x00030003u << p, magic);
-    } else {
-      const int P = 4 * fi + j;
-      if (P < 30) {
-        const int fld = P % 5;
-        const uint32_t q = fld < 3 ? w[P / 5] : w[P / 5] >> 9;
-        p = 3 * (fld < 3 ? fld : fld - 3);
-        return and_or_b32(q, 0x00070007u << p, magic);
-      }
-      const int d0 = 3 * (P - 30);
-      p = 0;
-      uint32_t t = and_or_b32(w[d0] >> 15, 0x00010001u, magic);
-      t = and_or_b32(w[d0 + 1] >> 14, 0x00020002u, t);
-      return and_or_b32(w[d0 + 2] >> 13, 0x00040004u, t);
+    constexpr uint32_t lowb = (1u << B) - 1u;
+    const int P = 4 * (2 * f + s) + j;
+    if (SB == 0 || P < NPF) {
+      const int o = B * (P % NF);
+      const uint32_t d = w[P / NF];
+      const bool in_place = o + B <= 10;
+      p = in_place ? o : 0;
+      return and_or_b32(in_place ? d : d >> o, (lowb << p) * 0x00010001u, magic);
     }
+    uint32_t t = magic;
+    p = 0;
+    if constexpr (SB > 0) {
+      // gather the spare bits of pair q, one run of bits per dword
+      const int q = P - NPF;
+#pragma unroll
+      for (int k = 0; k < B;) {
+        const int g = q * B + k, d = g / SB, off = g % SB;
+        const int n = min(B - k, SB - off);  // bits of u in this dword
+        const int pos = NF * B + off;         // their first bit in each half
+        t = and_or_b32(w[d] >> (pos - k), (((1u << n) - 1u) << k) * 0x00010001u, t);
+        k += n;
+      }
+    }
+    return t;
   }
   // fp16(code * scale): (1024 + 2^p u) 2^-p - (1024 2^-p + 2^(b-1)) is the
   // code, exact (one packed fma); one packed multiply by the scale rounds
@@ -375,10 +320,10 @@ struct WTileP {
 };
 template <> struct WTile<MOE_I2_G32> : WTileP<2> {};
 template <> struct WTile<MOE_I3_G32> : WTileP<3> {};
-template <> struct WTile<MOE_I5_G32> : WTileB<5> {};
-template <> struct WTile<MOE_I6_G32> : WTileB<6> {};
-template <> struct WTile<MOE_I7_G32> : WTileB<7> {};
-template <> struct WTile<MOE_I8_G32> : WTileB<8> {};
+template <> struct WTile<MOE_I5_G32> : WTileP<5> {};
+template <> struct WTile<MOE_I6_G32> : WTileP<6> {};
+template <> struct WTile<MOE_I7_G32> : WTileP<7> {};
+template <> struct WTile<MOE_I8_G32> : WTileP<8> {};
 
 // Gate/up of int4 (and b-bit group-32) layers runs fp16 MFMA on the fp16
 // copy of x: their code -> fp16 conversion costs fewer VALU ops than bf16,
