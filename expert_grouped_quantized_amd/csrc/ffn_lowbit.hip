@@ -2,7 +2,7 @@
 // experts coded at 2, 3, 5, 6, 7 or 8 bits with one fp16 scale per 32 weights
 // along K (TandemLLM roadmap, "A mixture-of-experts model, and what is left":
 // MoE kernels over several code widths).  Same kernels as int4; only the
-// weight tile and its dequantization differ (WTileB).
+// weight tile and its dequantization differ (WTileP).
 #include "ffn_kernels.h"
 
 namespace moe {
