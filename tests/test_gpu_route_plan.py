@@ -106,6 +106,7 @@ SMALL = [
     _cfg("rp_E64_k32", 3, E=64, k=32, n_shared=0, Fs=0),  # the largest k
     _cfg("rp_i3_E200", 4, E=200, k=10, expert=W.IG32[3]),
     _cfg("rp_mx_E40", 5, E=40, k=5, expert=W.MXFP4),  # no fp16 copy of x
+    _cfg("rp_zipf_bias_E512", 6, E=512, k=10, zipf=True),  # router bias, skewed routing
 ]
 
 
