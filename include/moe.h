@@ -28,11 +28,13 @@
  *
  * Conventions for every call below:
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     never allocates device memory and keeps no device state between calls.
+ *     never allocates device memory; what a call leaves behind lives in the
+ *     caller's buffers (moe_route_plan's counters in the workspace, zero
+ *     between calls), apart from moe_grouped_ffn_noalloc's static scratch.
  *   - Device calls (moe_route*, moe_permute, moe_grouped_ffn, moe_combine)
  *     take device pointers and a hipStream_t passed as `void* stream` (NULL =
- *     the null stream).  They only enqueue work: nothing synchronizes, so the
- *     four calls can be captured in one HIP graph.  They run on the device
+ *     the null stream).  They only enqueue work: nothing synchronizes, so a
+ *     layer's calls can be captured in one HIP graph.  They run on the device
  *     current to the calling thread.
  *   - Errors: arguments are checked on the host before anything is enqueued.
  *     A failed check returns a negative moe_status and sets a thread-local
