@@ -107,6 +107,8 @@ SMALL = [
     _cfg("rp_i3_E200", 4, E=200, k=10, expert=W.IG32[3]),
     _cfg("rp_mx_E40", 5, E=40, k=5, expert=W.MXFP4),  # no fp16 copy of x
     _cfg("rp_zipf_bias_E512", 6, E=512, k=10, zipf=True),  # router bias, skewed routing
+    _cfg("rp_E1_k1", 7, E=1, k=1, n_shared=0, Fs=0),        # one expert: a dense layer
+    _cfg("rp_E20_k3_bf16", 8, E=20, k=3, expert=W.BF16, shared=W.BF16),
 ]
 
 
